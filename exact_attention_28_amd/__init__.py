@@ -1,0 +1,158 @@
+"""Exact attention on AMD Instinct MI355X (gfx950): thin Python binding.
+
+The work is done by ``libattn.so`` (hand-written HIP kernels behind the C ABI
+of ``include/attn.h``).  This module only marshals torch tensors (device
+memory) and the current HIP stream into those calls; it computes nothing
+itself and has no fallback: if the library is missing or the tensors are not
+on a GPU, the call raises.
+
+Entry points (same names as the C ABI):
+  attn_fwd(q, k, v, causal=False, scale=None, rope_base=0.0, o=None, lse=None)
+  attn_decode_splitkv(q, kcache, vcache, seqlens, num_splits, scale=None, ...)
+  rope_apply(x, pos_offset=0, rope_base=10000.0)
+  attn_decode_workspace_bytes(B, Hq, D, num_splits)
+"""
+import ctypes
+import math
+import os
+
+import torch  # loads the HIP runtime that libattn.so then binds to
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_EMPTY_KV = 0, -1, -2, -3, -4
+EXPORTS = ("attn_fwd", "attn_decode_workspace_bytes", "attn_decode_splitkv", "rope_apply",
+           "attn_last_error")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+def load():
+    """Load libattn.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with exact_attention_28_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, i, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
+    lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp]
+    lib.attn_decode_splitkv.restype = i
+    lib.rope_apply.argtypes = [vp, i, i, i, i, i, f, i, vp]
+    lib.rope_apply.restype = i
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def last_error():
+    return load().attn_last_error().decode()
+
+
+def _check(code):
+    if code != ATTN_OK:
+        raise AttnError(code, last_error())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on a GPU device")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def attn_fwd(q, k, v, causal=False, scale=None, rope_base=0.0, o=None, lse=None, stream=None,
+             want_lse=True):
+    """O, LSE = exact attention.  q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (bf16 or fp32).
+
+    Returns (o [B,Sq,Hq,D] in q's dtype, lse [B,Hq,Sq] fp32 or None)."""
+    _need_gpu(q, k, v, o, lse)
+    B, Sq, Hq, D = q.shape
+    Bk, Skv, Hkv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Skv, D,
+                           int(bool(causal)), float(scale), float(rope_base), _dtype_code(q),
+                           _stream(stream)))
+    return o, lse
+
+
+def attn_decode_workspace_bytes(B, Hq, D, num_splits):
+    return int(load().attn_decode_workspace_bytes(B, Hq, D, num_splits))
+
+
+def attn_decode_splitkv(q, kcache, vcache, seqlens, num_splits, scale=None, o=None, lse=None,
+                        workspace=None, stream=None, want_lse=True):
+    """Split-KV decode.  q [B,Hq,D] bf16, caches [B,Smax,Hkv,D] bf16, seqlens [B] int32.
+
+    Returns (o [B,Hq,D] bf16, lse [B,Hq] fp32 or None)."""
+    _need_gpu(q, kcache, vcache, seqlens, o, lse, workspace)
+    B, Hq, D = q.shape
+    Bk, Smax, Hkv, Dk = kcache.shape
+    if tuple(vcache.shape) != tuple(kcache.shape) or Bk != B or Dk != D:
+        raise ValueError("shape mismatch between q and the caches")
+    if seqlens.dtype != torch.int32 or seqlens.numel() != B:
+        raise ValueError("seqlens must be int32 [B]")
+    if q.dtype != torch.bfloat16 or kcache.dtype != torch.bfloat16 or vcache.dtype != torch.bfloat16:
+        raise TypeError("decode takes bf16 q and caches")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace is not None and workspace.numel() * workspace.element_size() < \
+            attn_decode_workspace_bytes(B, Hq, D, num_splits):
+        raise ValueError("workspace too small")
+    _check(load().attn_decode_splitkv(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(o),
+                                      B, Hq, Hkv, D, int(num_splits), float(scale), Smax,
+                                      _ptr(lse), _ptr(workspace), _stream(stream)))
+    return o, lse
+
+
+def rope_apply(x, pos_offset=0, rope_base=10000.0, stream=None):
+    """Rotate x [B,S,H,D] (bf16 or fp32) in place at positions pos_offset + t."""
+    _need_gpu(x)
+    B, S, H, D = x.shape
+    _check(load().rope_apply(_ptr(x), B, S, H, D, int(pos_offset), float(rope_base),
+                             _dtype_code(x), _stream(stream)))
+    return x

@@ -1,0 +1,226 @@
+// attn_api.hip — the C ABI declared in include/attn.h: argument validation,
+// library-owned device buffers, and kernel dispatch.  Host code only.
+//
+// Validation rules follow the pages' constructors and error types:
+// scirs2-neural 0.4.4 src/layers/grouped_query_attention.rs
+// (GroupedQueryAttention::new rejects zero sizes and a head count that is not a
+// multiple of the kv-head count; RotaryPositionEmbedding::new rejects an odd
+// head dim), whisper-apr 0.3.1 src/model/lfm2/gqa.rs (GqaConfig::validate),
+// oxibonsai-model 0.1.4 src/layers/flash_decode.rs (FlashDecodeError::EmptyKv
+// for zero keys).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+
+#include "attn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return ATTN_OK;
+}
+
+// Library-owned device buffers of one device: grow-only, kept until exit.
+struct DevBuffers {
+  void* rope_tab = nullptr;
+  size_t rope_tab_bytes = 0;
+  void* kstage = nullptr;
+  size_t kstage_bytes = 0;
+  void* dec_ws = nullptr;
+  size_t dec_ws_bytes = 0;
+};
+
+std::mutex g_mu;
+std::map<int, DevBuffers> g_dev;
+
+// Make *p hold at least `need` bytes on the current device.
+int grow(void** p, size_t* cap, size_t need, const char* what) {
+  if (*cap >= need && *p != nullptr) return ATTN_OK;
+  if (*p != nullptr) {
+    hipError_t e = hipFree(*p);  // synchronises the device before the buffer goes
+    *p = nullptr;
+    *cap = 0;
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipFree(%s): %s", what, hipGetErrorString(e));
+  }
+  hipError_t e = hipMalloc(p, need);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    return fail(ATTN_ERR_HIP, "hipMalloc(%s, %zu bytes): %s", what, need, hipGetErrorString(e));
+  }
+  *cap = need;
+  return ATTN_OK;
+}
+
+DevBuffers* buffers(int* status) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *status = fail(ATTN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  *status = ATTN_OK;
+  return &g_dev[dev];
+}
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.f; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int Sq, int Skv, int D, int causal, float scale, float rope_base,
+             int dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID, "attn_fwd: null q, k, v or o");
+  if (Skv == 0) return fail(ATTN_ERR_EMPTY_KV, "attn_fwd: no keys (Skv == 0)");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1)
+    return fail(ATTN_ERR_INVALID, "attn_fwd: sizes must be >= 1 (B=%d Hq=%d Hkv=%d Sq=%d Skv=%d D=%d)",
+                B, Hq, Hkv, Sq, Skv, D);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_INVALID, "attn_fwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID, "attn_fwd: causal must be 0 or 1");
+  if (!finite_pos(scale)) return fail(ATTN_ERR_INVALID, "attn_fwd: scale must be finite and > 0");
+  if (std::isnan(rope_base) || std::isinf(rope_base))
+    return fail(ATTN_ERR_INVALID, "attn_fwd: rope_base must be finite");
+  const bool rope = rope_base > 0.f;
+  if (rope && D % 2 != 0) return fail(ATTN_ERR_INVALID, "attn_fwd: RoPE needs an even head dim");
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_INVALID, "attn_fwd: unknown dtype %d", dtype);
+  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: D=%d (built: 64, 128)", D);
+  if (rope && Sq > Skv)
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "attn_fwd: RoPE with Sq > Skv would place queries at negative positions");
+  if ((long long)B * Hq * ((Sq + 15) / 16) > 0x7fffffffLL || B > 65535 || Hq > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: grid too large");
+
+  const double2* tab = nullptr;
+  const void* kin = k;
+  if (rope) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    int st;
+    DevBuffers* db = buffers(&st);
+    if (!db) return st;
+    const size_t tab_bytes = (size_t)Skv * (D / 2) * sizeof(double2);
+    if ((st = grow(&db->rope_tab, &db->rope_tab_bytes, tab_bytes, "rope table")) != ATTN_OK)
+      return st;
+    tab = static_cast<const double2*>(db->rope_tab);
+    hipError_t e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), 0, Skv, D,
+                                            (double)rope_base, stream);
+    if (e != hipSuccess) return hip_status(e, "attn_fwd: rope table launch");
+    if (dtype == ATTN_BF16) {
+      const size_t kb = (size_t)B * Skv * Hkv * D * 2;
+      if ((st = grow(&db->kstage, &db->kstage_bytes, kb, "rotated K")) != ATTN_OK) return st;
+      e = xattn::launch_rope_rotate(k, db->kstage, B, Skv, Hkv, D, tab, 1, stream);
+      if (e != hipSuccess) return hip_status(e, "attn_fwd: K rotation launch");
+      kin = db->kstage;
+    }
+  }
+  hipError_t e;
+  if (dtype == ATTN_BF16)
+    e = xattn::launch_fwd_bf16(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab,
+                               stream);
+  else
+    e = xattn::launch_fwd_f32(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab,
+                              stream);
+  return hip_status(e, "attn_fwd: kernel launch");
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
+  if (B < 1 || Hq < 1 || D < 1 || num_splits < 1) return 0;
+  return xattn::decode_workspace_bytes(B, Hq, D, num_splits);
+}
+
+int attn_decode_splitkv(const void* q, const void* kcache, const void* vcache,
+                        const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
+                        int num_splits, float scale, int max_seqlen, float* lse,
+                        void* workspace, hipStream_t stream) {
+  if (!q || !kcache || !vcache || !seqlens || !o)
+    return fail(ATTN_ERR_INVALID, "attn_decode_splitkv: null q, kcache, vcache, seqlens or o");
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1)
+    return fail(ATTN_ERR_INVALID, "attn_decode_splitkv: sizes must be >= 1");
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_INVALID, "attn_decode_splitkv: Hq=%d is not a multiple of Hkv=%d", Hq,
+                Hkv);
+  if (num_splits < 1 || num_splits > 64)
+    return fail(ATTN_ERR_INVALID, "attn_decode_splitkv: num_splits=%d outside [1, 64]",
+                num_splits);
+  if (max_seqlen < 1) return fail(ATTN_ERR_INVALID, "attn_decode_splitkv: max_seqlen < 1");
+  if (!finite_pos(scale))
+    return fail(ATTN_ERR_INVALID, "attn_decode_splitkv: scale must be finite and > 0");
+  if (D != 64 && D != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_splitkv: D=%d (built: 64, 128)", D);
+  if (B > 65535 || Hq > 65535 || (long long)B * Hq > 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_splitkv: grid too large");
+
+  void* ws = workspace;
+  if (ws == nullptr) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    int st;
+    DevBuffers* db = buffers(&st);
+    if (!db) return st;
+    if ((st = grow(&db->dec_ws, &db->dec_ws_bytes,
+                   xattn::decode_workspace_bytes(B, Hq, D, num_splits), "decode workspace")) !=
+        ATTN_OK)
+      return st;
+    ws = db->dec_ws;
+  }
+  hipError_t e = xattn::launch_decode(q, kcache, vcache, seqlens, o, lse, B, Hq, Hkv, D,
+                                      num_splits, scale, max_seqlen, ws, stream);
+  return hip_status(e, "attn_decode_splitkv: kernel launch");
+}
+
+int rope_apply(void* x, int B, int S, int H, int D, int pos_offset, float rope_base, int dtype,
+               hipStream_t stream) {
+  if (!x) return fail(ATTN_ERR_INVALID, "rope_apply: null x");
+  if (B < 1 || S < 1 || H < 1 || D < 1) return fail(ATTN_ERR_INVALID, "rope_apply: sizes must be >= 1");
+  if (D % 2 != 0) return fail(ATTN_ERR_INVALID, "rope_apply: RoPE head_dim must be even (D=%d)", D);
+  if (pos_offset < 0) return fail(ATTN_ERR_INVALID, "rope_apply: pos_offset < 0");
+  if ((long long)pos_offset + S > 0x7fffffffLL)
+    return fail(ATTN_ERR_INVALID, "rope_apply: positions overflow");
+  if (!finite_pos(rope_base)) return fail(ATTN_ERR_INVALID, "rope_apply: rope_base must be finite and > 0");
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_INVALID, "rope_apply: unknown dtype %d", dtype);
+  if (D > 256) return fail(ATTN_ERR_UNSUPPORTED, "rope_apply: D=%d (built: up to 256)", D);
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  int st;
+  DevBuffers* db = buffers(&st);
+  if (!db) return st;
+  const size_t tab_bytes = (size_t)S * (D / 2) * sizeof(double2);
+  if ((st = grow(&db->rope_tab, &db->rope_tab_bytes, tab_bytes, "rope table")) != ATTN_OK)
+    return st;
+  hipError_t e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), pos_offset, S, D,
+                                          (double)rope_base, stream);
+  if (e != hipSuccess) return hip_status(e, "rope_apply: table launch");
+  e = xattn::launch_rope_rotate(x, x, B, S, H, D, static_cast<const double2*>(db->rope_tab),
+                                dtype, stream);
+  return hip_status(e, "rope_apply: kernel launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// kernels.h — host-side launchers of the gfx950 kernels (internal to libattn.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace xattn {
+
+// Prefill: q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D], o like q, lse [B,Hq,Sq] (nullable).
+// rope_tab: table rows for positions [0, Skv); query row i uses row Skv-Sq+i.
+// bf16 rotates only the queries in the kernel (keys arrive rotated); fp32
+// rotates queries and keys.  Null disables rotation.
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                           float scale, const double2* rope_tab, hipStream_t stream);
+hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                          float scale, const double2* rope_tab, hipStream_t stream);
+
+// RoPE: row t of the table holds (cos, sin)((pos0 + t) / base^(2i/D)) for
+// t < npos, i < D/2, in fp64.
+hipError_t launch_rope_table(double2* tab, int pos0, int npos, int D, double base,
+                             hipStream_t stream);
+// Rotate x [B,S,H,D] (dtype 0 fp32 / 1 bf16) into y (y may equal x); token t
+// uses table row t.
+hipError_t launch_rope_rotate(const void* x, void* y, int B, int S, int H, int D,
+                              const double2* tab, int dtype, hipStream_t stream);
+
+// Decode: split pass into the workspace, then the merge pass.
+size_t decode_workspace_bytes(int B, int Hq, int D, int num_splits);
+hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int* seqlens,
+                         void* o, float* lse, int B, int Hq, int Hkv, int D, int num_splits,
+                         float scale, int max_seqlen, void* workspace, hipStream_t stream);
+
+}  // namespace xattn

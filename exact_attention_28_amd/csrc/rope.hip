@@ -1,0 +1,116 @@
+// rope.hip — rotary position embedding for gfx950.
+//
+// Interleaved pair rotation of scirs2-neural 0.4.4 (src/layers/
+// grouped_query_attention.rs, RotaryPositionEmbedding::apply): pair (2i, 2i+1)
+// of a token at position p turns by theta = p / base^(2i/D); the page evaluates
+// theta, cos and sin in f64.  Here the (cos, sin) table is built once in fp64 on
+// the device and the rotation itself is done in fp64, then rounded once to the
+// storage format (nearest, ties to even).
+#include "common.h"
+#include "kernels.h"
+
+namespace xattn {
+
+// Row t of the table holds (cos, sin) of theta = (pos0 + t) / base^(2i/D), i < D/2.
+__global__ void rope_table_kernel(double2* __restrict__ tab, int pos0, int npos, int half, int D,
+                                  double base) {
+  const long long n = (long long)npos * half;
+  for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < n;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int t = (int)(idx / half), i = (int)(idx % half);
+    const double theta = (double)(pos0 + t) / pow(base, (2.0 * i) / (double)D);
+    double s, c;
+    sincos(theta, &s, &c);
+    tab[idx] = make_double2(c, s);
+  }
+}
+
+hipError_t launch_rope_table(double2* tab, int pos0, int npos, int D, double base,
+                             hipStream_t stream) {
+  const int half = D / 2;
+  const long long n = (long long)npos * half;
+  const int threads = 256;
+  long long blocks = (n + threads - 1) / threads;
+  if (blocks > 65535) blocks = 65535;
+  if (blocks < 1) blocks = 1;
+  rope_table_kernel<<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(tab, pos0, npos, half, D,
+                                                                         base);
+  return hipGetLastError();
+}
+
+// bf16, 4 pairs (16 bytes) per thread; needs D % 8 == 0.
+__global__ void rope_rotate_bf16x8(const u16* x, u16* y,
+                                   long long nchunks, int S, int H, int D,
+                                   const double2* __restrict__ tab) {
+  const int cpr = D / 8;  // 16-byte chunks per head row
+  const int half = D / 2;
+  for (long long c = blockIdx.x * (long long)blockDim.x + threadIdx.x; c < nchunks;
+       c += (long long)gridDim.x * blockDim.x) {
+    const long long row = c / cpr;  // (b, t, h) flattened
+    const int part = (int)(c % cpr);
+    const int t = (int)((row / H) % S);
+    const u32x4 w = *reinterpret_cast<const u32x4*>(x + c * 8);
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double2 cs = tab[(long long)t * half + part * 4 + e];
+      double r0, r1;
+      rotate_pair((double)bf16_lo(w[e]), (double)bf16_hi(w[e]), cs, r0, r1);
+      r[e] = f64_to_bf16_bits(r0) | (f64_to_bf16_bits(r1) << 16);
+    }
+    *reinterpret_cast<u32x4*>(y + c * 8) = r;
+  }
+}
+
+// Any even D: one pair per thread, bf16 (a uint32 holds the pair) or fp32.
+// x and y may alias (in-place rotation): each thread reads, then writes, only its own pair.
+template <bool BF16>
+__global__ void rope_rotate_pair(const void* xv, void* yv,
+                                 long long npairs, int S, int H, int D,
+                                 const double2* __restrict__ tab) {
+  const int half = D / 2;
+  for (long long pidx = blockIdx.x * (long long)blockDim.x + threadIdx.x; pidx < npairs;
+       pidx += (long long)gridDim.x * blockDim.x) {
+    const long long row = pidx / half;
+    const int i = (int)(pidx % half);
+    const int t = (int)((row / H) % S);
+    const double2 cs = tab[(long long)t * half + i];
+    double r0, r1;
+    if (BF16) {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(xv)[pidx];
+      rotate_pair((double)bf16_lo(w), (double)bf16_hi(w), cs, r0, r1);
+      reinterpret_cast<uint32_t*>(yv)[pidx] = f64_to_bf16_bits(r0) | (f64_to_bf16_bits(r1) << 16);
+    } else {
+      const float2 w = reinterpret_cast<const float2*>(xv)[pidx];
+      rotate_pair((double)w.x, (double)w.y, cs, r0, r1);
+      reinterpret_cast<float2*>(yv)[pidx] = make_float2((float)r0, (float)r1);
+    }
+  }
+}
+
+hipError_t launch_rope_rotate(const void* x, void* y, int B, int S, int H, int D,
+                              const double2* tab, int dtype, hipStream_t stream) {
+  const long long rows = (long long)B * S * H;
+  const int threads = 256;
+  const long long max_blocks = 256LL * 8 * 4;  // a few resident waves per SIMD, grid-stride
+  if (dtype == 1 && D % 8 == 0) {
+    const long long n = rows * (D / 8);
+    long long blocks = (n + threads - 1) / threads;
+    if (blocks > max_blocks) blocks = max_blocks;
+    rope_rotate_bf16x8<<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
+        static_cast<const u16*>(x), static_cast<u16*>(y), n, S, H, D, tab);
+  } else {
+    const long long n = rows * (D / 2);
+    long long blocks = (n + threads - 1) / threads;
+    if (blocks > max_blocks) blocks = max_blocks;
+    if (dtype == 1)
+      rope_rotate_pair<true><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
+          x, y, n, S, H, D, tab);
+    else
+      rope_rotate_pair<false><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
+          x, y, n, S, H, D, tab);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace xattn

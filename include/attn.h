@@ -1,0 +1,154 @@
+/*
+ * attn.h — C ABI of the exact-attention library for AMD Instinct MI355X (gfx950).
+ *
+ * Exact scaled-dot-product attention O = softmax(scale * Q K^T) V computed by
+ * tiles with an online softmax (a running row maximum m and row sum l, rescaled
+ * per key/value tile), with causal masking, grouped-query heads, rotary position
+ * embedding on Q and K, and flash-decoding (split-KV partial results merged by
+ * log-sum-exp).
+ *
+ * Definitions follow these docs.rs source pages:
+ *   [FA]  scirs2-neural 0.4.3, src/layers/flash_attention.rs
+ *   [GQA] scirs2-neural 0.4.4, src/layers/grouped_query_attention.rs
+ *   [WH]  whisper-apr 0.3.1, src/model/attention_generated.rs
+ *   [FD]  oxibonsai-model 0.1.4, src/layers/flash_decode.rs
+ *   [LF]  whisper-apr 0.3.1, src/model/lfm2/gqa.rs
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never frees caller memory.  Tensors are dense and contiguous.
+ *  - Calls are asynchronous on `stream` (0 = the null stream): arguments are
+ *    validated synchronously on the host before anything is enqueued, then
+ *    the kernels are launched and the call returns without synchronising.
+ *  - Return value: ATTN_OK (0) or a negative attn_status_t; on error nothing is
+ *    enqueued and attn_last_error() describes the problem.  Nothing throws
+ *    across the ABI.
+ *  - Library-owned device buffers (RoPE tables, rotated-K staging, the default
+ *    decode workspace) are allocated on first need, grow only, and are kept per
+ *    device until the process ends; calls that use them concurrently on
+ *    different streams of one device must be ordered by the caller.
+ */
+#ifndef EXACT_ATTN_H
+#define EXACT_ATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_F32 = 0,  /* IEEE binary32 */
+  ATTN_BF16 = 1, /* bfloat16 (8 significant bits) */
+} attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = -1,     /* null pointer, size < 1, Hq not a multiple of Hkv,
+                                odd D with RoPE, scale not finite or <= 0, ... */
+  ATTN_ERR_UNSUPPORTED = -2, /* valid but not built: D not 64/128, dtype, ... */
+  ATTN_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+  ATTN_ERR_EMPTY_KV = -4,    /* zero keys ([FD] FlashDecodeError::EmptyKv) */
+} attn_status_t;
+
+/*
+ * attn_fwd — exact attention forward pass with per-row log-sum-exp.
+ *
+ * Computes, for batch b, query head h, query row i and d < D:
+ *   g        = h / (Hq / Hkv)                         (contiguous GQA groups:
+ *                                                      [GQA] forward loop, [LF]
+ *                                                      fn attention_scalar)
+ *   s_ij     = scale * <q~[b,i,h,:], k~[b,j,g,:]>     ([FA] compute_block_scores)
+ *   s_ij     = -inf  if causal and j > i + (Skv - Sq)  ([FA] apply_causal_mask for
+ *                                                      Sq == Skv; bottom-right
+ *                                                      alignment otherwise, the
+ *                                                      cached-generation rule of
+ *                                                      [GQA] forward_with_cache)
+ *   O[b,i,h,d] = sum_j exp(s_ij - m_i) v[b,j,g,d] / l_i,  m_i = max_j s_ij,
+ *   l_i = sum_j exp(s_ij - m_i),  lse[b,h,i] = m_i + ln l_i
+ * by the tiled forward with online softmax of [FA] flash_attention_forward /
+ * online_softmax_update.  A row with no visible key (causal with Sq > Skv)
+ * gets O = 0 and lse = -inf.
+ * q~, k~ are Q and K after rotary embedding when rope_base > 0 ([GQA]
+ * RotaryPositionEmbedding::apply: pair (2i, 2i+1) rotated by the angle
+ * pos / rope_base^(2i/D)), with query row i at position Skv - Sq + i and key j
+ * at position j; the rotation is evaluated in fp64 and rounded to `dtype`
+ * (nearest, ties to even) before the dot products.  V is not rotated.
+ *
+ * Arguments:
+ *   q    [B, Sq, Hq, D]  dtype          k, v [B, Skv, Hkv, D] dtype
+ *   o    [B, Sq, Hq, D]  dtype (output) lse  [B, Hq, Sq] fp32 (output; may be NULL)
+ *   B, Hq, Hkv, Sq, Skv, D >= 1; Hq % Hkv == 0; D in {64, 128}
+ *   causal: 0 or 1;  scale: finite and > 0, used as given (the pages' default
+ *   is 1/sqrt(D));  rope_base: > 0 enables RoPE (D even), <= 0 disables it
+ *   dtype: ATTN_BF16 (bf16 MFMA, fp32 accumulation) or ATTN_F32 (fp32 throughout)
+ * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_EMPTY_KV (Skv == 0),
+ *   ATTN_ERR_HIP.  With rope_base > 0 and bf16, the call may allocate the
+ *   library's rotated-K staging buffer (B*Skv*Hkv*D*2 bytes) and RoPE table.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int Sq, int Skv, int D, int causal, float scale, float rope_base,
+             int dtype, hipStream_t stream);
+
+/*
+ * attn_decode_workspace_bytes — size of the workspace attn_decode_splitkv needs
+ * for the per-split partial outputs and log-sum-exps: B*Hq*num_splits*(D+1)*4
+ * bytes rounded up to 256.  Returns 0 for invalid sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
+
+/*
+ * attn_decode_splitkv — flash-decoding of one query token per sequence.
+ *
+ * For batch b and query head h (kv head g = h / (Hq/Hkv)), attends q[b,h,:]
+ * to the first L_b = seqlens[b] positions of the caches, with no mask
+ * ([LF] fn attention_cached).  The positions [0, L_b) are split into
+ * num_splits chunks; each chunk yields a normalised partial output and its
+ * log-sum-exp ([FD] fn flash_decode_tile); a second pass merges the chunks by
+ * log-sum-exp, dropping empty chunks ([FD] fn combine_tile_outputs).  The
+ * result equals exact attention over all L_b positions for any split.
+ * L_b == 0 gives O = 0 and lse = -inf.
+ *
+ * Arguments:
+ *   q       [B, Hq, D] bf16
+ *   kcache, vcache [B, max_seqlen, Hkv, D] bf16, token-major ([FD]
+ *           flash_decode_multi_head layout; [LF] KvCache); rows >= L_b are
+ *           never read
+ *   seqlens [B] int32 in device memory, 0 <= seqlens[b] <= max_seqlen
+ *           (a precondition: it is not checked on the host because the values
+ *           live on the device; larger values are clamped to max_seqlen)
+ *   o       [B, Hq, D] bf16 (output);  lse [B, Hq] fp32 (output, may be NULL)
+ *   B, Hq, Hkv >= 1; Hq % Hkv == 0; D in {64, 128}; 1 <= num_splits <= 64;
+ *   max_seqlen >= 1; scale finite and > 0
+ *   workspace: device buffer of attn_decode_workspace_bytes(B, Hq, D,
+ *           num_splits) bytes, or NULL to use a library-owned buffer
+ * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP.
+ */
+int attn_decode_splitkv(const void* q, const void* kcache, const void* vcache,
+                        const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
+                        int num_splits, float scale, int max_seqlen, float* lse,
+                        void* workspace, hipStream_t stream);
+
+/*
+ * rope_apply — rotary position embedding, in place ([GQA]
+ * RotaryPositionEmbedding::apply with its position_offset argument).
+ *
+ * x [B, S, H, D] of dtype; token t is at position pos_offset + t; pair
+ * (2i, 2i+1) is rotated by pos / rope_base^(2i/D), evaluated in fp64 and
+ * rounded to dtype (nearest, ties to even).
+ *   B, S, H >= 1; D even, 2 <= D <= 256; pos_offset >= 0; rope_base > 0
+ * Errors: ATTN_ERR_INVALID (odd D: "RoPE head_dim must be even" in [GQA]),
+ *   ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP.
+ */
+int rope_apply(void* x, int B, int S, int H, int D, int pos_offset, float rope_base, int dtype,
+               hipStream_t stream);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTN_H */

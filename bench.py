@@ -1,0 +1,243 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step is one pass of the whole path on resident synthetic inputs:
+  * prefill: attn_fwd on the LFM2-2.6B-shaped GQA workload (B=4, Hq=32,
+    Hkv=8, S=4096, D=64, causal, RoPE base 10000, bf16) — RoPE table, key
+    rotation and the fused attention kernel;
+  * decode: attn_decode_splitkv on the split-KV workload (B=16, Hq=32, Hkv=8,
+    D=128, bf16 cache of 32768 positions, lengths U[1024, 32768]) — split
+    pass and LSE merge — at the split count that measured fastest among
+    4, 8, 16, 32, 64 before the timed region.
+
+Printed: one JSON line.  `value` is the prefill throughput in TFLOP/s
+(algorithmic flops 4*B*Hq*S*S*D/2 over the event-timed attn_fwd call); the
+decode KV-read bandwidth and both fractions of peak sit beside it.  The
+`roofline` object is for the dominant kernel (the fused prefill kernel),
+timed alone with HIP events on its stream.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import exact_attention_28_amd as xa  # noqa: E402
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "attention fwd TFLOP/s + decode KV GB/s, as % of MI355X MFMA/HBM peak"
+KERNEL_SOURCES = ("fwd_bf16.hip", "common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_lfm2_gqa_prefill_s4096_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_28_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(launch_flops_bytes):
+    """HBM traffic per launch of the prefill kernel from the committed
+    rocprofv3 counter summary, or None when the kernel changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for ln in open(TRAFFIC_FILE):
+        if ":" in ln and not ln.startswith("#"):
+            k, v = ln.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def timed(fn, reps, stream):
+    """Mean duration (ms) of fn() over reps, bracketed by HIP events on stream."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+
+
+def cpu_baseline(prefill, dec_inputs, budget_s):
+    """The fp64 oracle as it stands, timed on this host on a bounded sample."""
+    import oracle
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    cfg = W.C4
+    q, k, v = prefill
+    units = list(range(threads))  # one (batch, head) per thread: whole 4096x4096 score matrix
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, causal=True, scale=cfg.scale, rope_base=cfg.rope_base,
+                    units=units, nthreads=threads)
+    t_pre = time.perf_counter() - t0
+    flops = cfg.flops / (cfg.B * cfg.Hq) * len(units)
+    out = {"value": flops / t_pre / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"LFM2 GQA prefill, {len(units)} of {cfg.B * cfg.Hq} (batch, head) units "
+                     f"(all 4096 query rows each), {t_pre:.1f} s"}
+    qd, kc, vc, sl = dec_inputs
+    dcfg = W.C5
+    n = 0
+    t0 = time.perf_counter()
+    kv_bytes = 0
+    while n < dcfg.B * dcfg.Hq and time.perf_counter() - t0 < budget_s / 3:
+        units = list(range(n, min(n + threads, dcfg.B * dcfg.Hq)))
+        oracle.decode(qd, kc, vc, sl, scale=dcfg.scale, units=units, nthreads=threads)
+        # each unit reads its kv head's L_b rows of K and V once
+        kv_bytes += sum(int(sl[u // dcfg.Hq]) * dcfg.D * 2 * 2 for u in units)
+        n += len(units)
+    t_dec = time.perf_counter() - t0
+    out["decode"] = {"value": kv_bytes / t_dec / 1e9, "unit": "GB/s",
+                     "sample": f"split-KV decode, {n} of {dcfg.B * dcfg.Hq} (batch, head) "
+                               f"units, {t_dec:.1f} s"}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    # ---- inputs, resident in HBM before anything is timed
+    pc, dc = W.C4, W.C5
+    log("generating inputs")
+    q_np, k_np, v_np = W.prefill_inputs(pc)
+    q, k, v = W.to_device(q_np), W.to_device(k_np), W.to_device(v_np)
+    o = torch.empty_like(q)
+    lse = torch.empty((pc.B, pc.Hq, pc.Sq), dtype=torch.float32, device="cuda")
+    dq_np, kc_np, vc_np, sl_np = W.decode_inputs(dc)
+    dq, kc, vc = W.to_device(dq_np), W.to_device(kc_np), W.to_device(vc_np)
+    sl = torch.from_numpy(sl_np).cuda()
+    do = torch.empty_like(dq)
+    dlse = torch.empty((dc.B, dc.Hq), dtype=torch.float32, device="cuda")
+    kv_bytes = int(sl_np.astype(np.int64).sum()) * dc.Hkv * dc.D * 2 * 2
+    ws = {ns: torch.empty(xa.attn_decode_workspace_bytes(dc.B, dc.Hq, dc.D, ns),
+                          dtype=torch.uint8, device="cuda") for ns in dc.splits}
+
+    def prefill():
+        xa.attn_fwd(q, k, v, causal=True, scale=pc.scale, rope_base=pc.rope_base, o=o, lse=lse)
+
+    def decode(ns):
+        xa.attn_decode_splitkv(dq, kc, vc, sl, ns, scale=dc.scale, o=do, lse=dlse,
+                               workspace=ws[ns])
+
+    # ---- warmup, and the split count for the decode half (outside the timed region)
+    log("warmup")
+    for _ in range(max(args.warmup, 1)):
+        prefill()
+        for ns in dc.splits:
+            decode(ns)
+    torch.cuda.synchronize()
+    split_ms = {ns: timed(lambda: decode(ns), 20, stream) for ns in dc.splits}
+    best_ns = min(split_ms, key=split_ms.get)
+    log("decode ms per split count:", {k_: round(v_, 4) for k_, v_ in split_ms.items()})
+
+    # ---- timed region: exactly `steps` steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        prefill()
+        ev[i][1].record(stream)
+        decode(best_ns)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    pre_tflops = pc.flops / (pre_ms * 1e-3) / 1e12
+    dec_gbps = kv_bytes / (dec_ms * 1e-3) / 1e9
+
+    # ---- the dominant kernel alone: the fused prefill kernel on the same shapes.
+    # Q and K are rotated once beforehand, so each attn_fwd call below is exactly
+    # one launch of the attention kernel (no table or key-rotation launches).
+    qr, kr = q.clone(), k.clone()
+    xa.rope_apply(qr, 0, pc.rope_base)
+    xa.rope_apply(kr, 0, pc.rope_base)
+    torch.cuda.synchronize()
+    kern_ms = timed(lambda: xa.attn_fwd(qr, kr, v, causal=True, scale=pc.scale, o=o, lse=lse),
+                    max(args.steps, 20), stream)
+    kern_tflops = pc.flops / (kern_ms * 1e-3) / 1e12
+    traffic = read_traffic(pc.io_bytes)
+
+    result = {
+        "metric": METRIC,
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "LFM2-2.6B-shaped GQA prefill B4 Hq32 Hkv8 S4096 D64 causal RoPE-10000 "
+                        "+ split-KV decode B16 Hq32 Hkv8 D128 Smax32768 L~U[1024,32768]",
+            "prefill": {"B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv, "S": pc.Sq, "D": pc.D,
+                        "causal": True, "rope_base": pc.rope_base, "seed": pc.seed},
+            "decode": {"B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv, "D": dc.D, "Smax": dc.Smax,
+                       "sum_lengths": int(sl_np.sum()), "num_splits": best_ns, "seed": dc.seed},
+            "parallelism": "single GPU",
+        },
+        "prefill": {"ms": round(pre_ms, 4), "tflops": round(pre_tflops, 2),
+                    "frac_of_mfma_peak": round(pre_tflops / PEAK_BF16_TFLOPS, 4)},
+        "decode": {"ms": round(dec_ms, 4), "GBps": round(dec_gbps, 1),
+                   "frac_of_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                   "kv_bytes": kv_bytes,
+                   "ms_by_splits": {str(k_): round(v_, 4) for k_, v_ in split_ms.items()}},
+        "roofline": {"kernel": "fwd_bf16_kernel<D=64,HPW=4,causal>", "bound": "mfma",
+                     "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
+                     "launch_ms": round(kern_ms, 4), "traffic": traffic},
+        "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1),
+                            "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                            "frac": round(dec_gbps / PEAK_HBM_GBPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        result["cpu_baseline"] = cpu_baseline((q_np, k_np, v_np), (dq_np, kc_np, vc_np, sl_np),
+                                              args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,9 +13,9 @@
 // sharing one kv head, batch).  The pass is HBM-bound (each cached K/V byte is
 // read once and feeds GW heads), so the kernel is built for bytes in flight:
 // D/8 lanes cover one 16-byte slice each of a token's K and V rows, a wave
-// takes 64/(D/8) tokens per step and UNROLL steps per iteration, all loads of
-// an iteration are issued before any is used.  Dot products are fp32 FMAs
-// reduced across the D/8 lanes with DPP; the online softmax keeps a reference
+// takes 64/(D/8) tokens per sub-step and kDecUnroll sub-steps per step, and
+// the loads of the next step are in flight while a step is consumed.  Dot
+// products are fp32 FMAs reduced across the D/8 lanes with DPP; the online softmax keeps a reference
 // maximum per lane and rescales only when a score exceeds it by more than 2^8
 // in the exp2 domain (the final O / l and m + log2 l are the same for any
 // reference, so this is exact).  Partial states of the lanes and waves of a
@@ -95,23 +95,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const u16* kb = Kc + (long long)b * Smax * tok_stride + (long long)kvh * D + sub * 8;
   const u16* vb = Vc + (long long)b * Smax * tok_stride + (long long)kvh * D + sub * 8;
 
-  for (int base = start; base < end; base += TOK_IT) {
-    u32x4 kr[kDecUnroll], vr[kDecUnroll];
-    int tok[kDecUnroll];
+  // Loads are never predicated: a token past `end` reads the last valid row
+  // (finite data) and gets probability 0, so no NaN beyond the length is read.
+  auto load_step = [&](int base, u32x4* kr, u32x4* vr) {
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
-      tok[u] = base + (w * kDecUnroll + u) * TPW + slot;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kr[u] = z;
-      vr[u] = z;
-      if (tok[u] < end) {
-        kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + tok[u] * tok_stride));
-        vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + tok[u] * tok_stride));
-      }
+      const int t = min(base + (w * kDecUnroll + u) * TPW + slot, end - 1);
+      kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + t * tok_stride));
+      vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + t * tok_stride));
     }
+  };
+  auto consume = [&](int base, const u32x4* kr, const u32x4* vr) {
     float sc[kDecUnroll][GW];
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
+      const bool live = base + (w * kDecUnroll + u) * TPW + slot < end;
       float kf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -124,7 +122,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) part = fmaf(qv[hh][e], kf[e], part);
         const float sv = group_sum<LPT>(part);
-        sc[u][hh] = (tok[u] < end) ? sv : -INFINITY;
+        sc[u][hh] = live ? sv : -INFINITY;
       }
     }
 #pragma unroll
@@ -157,6 +155,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(p, vf[e], acc[hh][e]);
       }
     }
+  };
+
+  // two register sets: the loads of step i+1 are in flight while step i is used
+  u32x4 ka[kDecUnroll], va[kDecUnroll], kb2[kDecUnroll], vb2[kDecUnroll];
+  if (start < end) load_step(start, ka, va);
+  for (int base = start; base < end; base += 2 * TOK_IT) {
+    if (base + TOK_IT < end) load_step(base + TOK_IT, kb2, vb2);
+    consume(base, ka, va);
+    if (base + TOK_IT >= end) break;
+    if (base + 2 * TOK_IT < end) load_step(base + 2 * TOK_IT, ka, va);
+    consume(base + TOK_IT, kb2, vb2);
   }
 
   // merge the token slots of the wave (lanes sub + LPT*slot, same sub)
@@ -206,17 +215,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   }
 }
 
-// One wave per (batch, query head): merge the splits by log-sum-exp.
+// One wave per (batch, query head): merge the splits by log-sum-exp.  Lane i
+// holds split i's lse and weight exp(lse_i - L); each lane then accumulates
+// its D/64 output elements over the splits.
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws_o,
                                                             const float* __restrict__ ws_lse,
                                                             u16* __restrict__ O,
                                                             float* __restrict__ LSE, int ns) {
+  constexpr int PER = D / 64;
   const long long bh = blockIdx.x;
   const int lane = threadIdx.x;
-  const float* lp = ws_lse + bh * ns;
-  const float li = (lane < ns) ? lp[lane] : -INFINITY;
-  const bool fin = li > -INFINITY && li < INFINITY;
+  const float li = (lane < ns) ? ws_lse[bh * ns + lane] : -INFINITY;
+  const bool fin = li > -INFINITY && li < INFINITY;  // empty splits carry -inf
   float M = fin ? li : -INFINITY;
 #pragma unroll
   for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
@@ -225,18 +236,17 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   for (int x = 32; x >= 1; x >>= 1) se += __shfl_xor(se, x);
   const bool any = M > -INFINITY;
   const float Lg = any ? M + __logf(se) : -INFINITY;
-  constexpr int PER = D / 64;
+  const float wl = fin ? __expf(li - Lg) : 0.f;
+
   float o[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  if (any) {
-    for (int i = 0; i < ns; ++i) {
-      const float lsi = lp[i];
-      if (!(lsi > -INFINITY && lsi < INFINITY)) continue;  // empty or masked split
-      const float wgt = __expf(lsi - Lg);
+  const float* op = ws_o + bh * ns * D + lane * PER;
+#pragma unroll 8
+  for (int i = 0; i < ns; ++i) {
+    const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
 #pragma unroll
-      for (int e = 0; e < PER; ++e) o[e] = fmaf(wgt, ws_o[(bh * ns + i) * D + lane * PER + e], o[e]);
-    }
+    for (int e = 0; e < PER; ++e) o[e] = fmaf(wi, op[(long long)i * D + e], o[e]);
   }
   if constexpr (PER == 2) {
     *reinterpret_cast<uint32_t*>(O + bh * D + lane * 2) = pack_bf16(o[0], o[1]);

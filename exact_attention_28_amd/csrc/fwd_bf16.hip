@@ -43,6 +43,9 @@
 
 namespace xattn {
 
+// Word 3 of a gfx9 buffer resource for raw (unformatted, stride 0) 32-bit access.
+constexpr int kBufferWord3 = 0x00020000;
+
 template <int D, int HPW, bool CAUSAL, bool ROPE>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
@@ -105,29 +108,38 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   const int first_q = p0 + off;  // smallest query position of the workgroup
 
-  const u16* kbase = K + (long long)kvh * D;
-  const u16* vbase = V + (long long)kvh * D;
-  const long long tok_stride = (long long)Hkv * D;
-  const long long bat_off = (long long)b * Skv * tok_stride;
+  // K and V of this (batch, kv head) through range-checked buffer resources:
+  // rows at or past Skv read as zero, offsets are 32-bit.
+  const long long head_base = (long long)b * Skv * Hkv * D + (long long)kvh * D;
+  const uint32_t nbytes = (uint32_t)(((long long)Skv * Hkv * D - (long long)kvh * D) * 2);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + head_base), (short)0, nbytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + head_base), (short)0, nbytes, kBufferWord3);
+  const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
+
+  uint32_t koff[K_LD], voff[V_LD];
+#pragma unroll
+  for (int i = 0; i < K_LD; ++i) {
+    const int cid = tid + 256 * i;
+    koff[i] = (uint32_t)(cid / KCH) * row_bytes + (uint32_t)(cid % KCH) * 16u;
+  }
+#pragma unroll
+  for (int i = 0; i < V_LD; ++i) {
+    const int cid = tid + 256 * i;
+    voff[i] = (uint32_t)(2 * (cid / KCH)) * row_bytes + (uint32_t)(cid % KCH) * 16u;
+  }
 
   u32x4 kreg[K_LD], vreg[2 * V_LD];
   auto gload = [&](int k0) {
+    const uint32_t t0 = (uint32_t)k0 * row_bytes;
 #pragma unroll
-    for (int i = 0; i < K_LD; ++i) {
-      const int cid = tid + 256 * i, row = cid / KCH, ch = cid % KCH, j = k0 + row;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (j < Skv) z = *reinterpret_cast<const u32x4*>(kbase + bat_off + j * tok_stride + ch * 8);
-      kreg[i] = z;
-    }
+    for (int i = 0; i < K_LD; ++i)
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[i] + t0, 0, 0);
 #pragma unroll
     for (int i = 0; i < V_LD; ++i) {
-      const int cid = tid + 256 * i, pr = cid / KCH, ch = cid % KCH, j = k0 + 2 * pr;
-      u32x4 z0 = {0u, 0u, 0u, 0u}, z1 = {0u, 0u, 0u, 0u};
-      if (j < Skv) z0 = *reinterpret_cast<const u32x4*>(vbase + bat_off + j * tok_stride + ch * 8);
-      if (j + 1 < Skv)
-        z1 = *reinterpret_cast<const u32x4*>(vbase + bat_off + (j + 1) * tok_stride + ch * 8);
-      vreg[2 * i] = z0;
-      vreg[2 * i + 1] = z1;
+      vreg[2 * i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i] + t0, 0, 0);
+      vreg[2 * i + 1] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i] + t0 + row_bytes, 0, 0);
     }
   };
   auto swrite = [&](int buf) {
@@ -142,9 +154,9 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
       const u32x4 a = vreg[2 * i], bb = vreg[2 * i + 1];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t wa = a[e >> 1], wb = bb[e >> 1];
-        const uint32_t word = (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u))
-                                      : ((wa & 0xffffu) | (wb << 16));
+        // element e of row 2pr (low half) and of row 2pr+1 (high half)
+        const uint32_t word = __builtin_amdgcn_perm(bb[e >> 1], a[e >> 1],
+                                                    (e & 1) ? 0x07060302u : 0x05040100u);
         *reinterpret_cast<uint32_t*>(&Vt[buf][(ch * 8 + e) * VST + 2 * pr]) = word;
       }
     }
@@ -155,12 +167,20 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  // m_run is a reference maximum (log2 domain): the true running maximum never
+  // exceeds it by more than 8, so every probability stays <= 2^8; it is moved
+  // (and O, l rescaled) only when a score would break that bound.  O / l and
+  // m_run + log2(l) do not depend on which reference is used.
   float m_run = -INFINITY, l_run = 0.f;
 
   if (ntiles > 0) {
     gload(0);
     swrite(0);
   }
+  // Everything the prologue loaded (the query fragment included) has landed:
+  // without this the loop head inherits a pending query load from the path
+  // with no tile and waits for every in-flight prefetch at each iteration.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
@@ -185,26 +205,39 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     // mask: key rows past Skv, and keys after the query under the causal rule
     const bool need_mask = (k0 + BN > Skv) || (CAUSAL && k0 + BN - 1 > first_q);
     if (need_mask) {
-      const int qlim = CAUSAL ? (pos + off) : 0x7fffffff;
+      const int qlim = CAUSAL ? min(pos + off, Skv - 1) : Skv - 1;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = k0 + blk * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (j >= Skv || j > qlim) s[blk][r] = -INFINITY;
+          if (j > qlim) s[blk][r] = -INFINITY;
         }
     }
 
     // online softmax for this lane's query column
-    float mx = s[0][0];
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mxs = mx * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mxs > m_run + 8.f)) {  // wave-uniform
+      const float m_new = fmaxf(m_run, mxs);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float ls = 0.f;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -214,13 +247,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
         s[blk][r] = p;
         ls += p;
       }
-    ls += __shfl_xor(ls, 32);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    l_run += ls;  // per half-wave partial; the halves are added after the loop
 
     // probabilities as bf16 B operands: chunk kc covers keys 16kc .. 16kc+15
     bf16x8 pf[4];
@@ -245,6 +272,11 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
 
     if (t + 1 < ntiles) swrite(buf ^ 1);
     __syncthreads();
+  }
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                     __float_as_uint(l_run), false, false);
+    l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
 
   if (qvalid) {

@@ -35,12 +35,22 @@ def _np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def check_bf16(o_gpu, lse_gpu, o_ref, lse_ref, what):
+def check_bf16(o_gpu, lse_gpu, o_ref, lse_ref, what, out_quant=False):
+    """bf16 bar: O max-abs 2e-2, O rel-L2 5e-3, LSE max-abs 1e-3.
+
+    out_quant: for test inputs outside the workloads' value range (|O| can
+    exceed 4), the bf16 rounding of the output alone is up to half an ulp,
+    2^-8 |O|, which is added to the absolute bound.
+    """
     o_gpu = np.asarray(o_gpu, np.float64)
     err = np.abs(o_gpu - o_ref)
+    if out_quant:
+        err = err - 2.0 ** -8 * np.abs(o_ref)
     rel = np.linalg.norm(o_gpu - o_ref) / max(np.linalg.norm(o_ref), 1e-30)
     assert np.isfinite(o_gpu).all(), f"{what}: non-finite output"
-    assert err.max() <= 2e-2, f"{what}: O max-abs {err.max():.3e}"
+    worst = np.unravel_index(np.argmax(err), err.shape)
+    assert err.max() <= 2e-2, (f"{what}: O max-abs {err.max():.3e} at {worst} "
+                               f"(got {o_gpu[worst]:.5f}, oracle {o_ref[worst]:.5f})")
     assert rel <= 5e-3, f"{what}: O rel-L2 {rel:.3e}"
     if lse_gpu is not None:
         fin = np.isfinite(lse_ref)
@@ -143,7 +153,7 @@ def test_bf16_variants(case):
     o, lse = run_fwd(q, k, v, causal, scale, rope)
     o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal=causal, scale=scale, rope_base=rope,
                                      nthreads=NTHREADS)
-    check_bf16(o, lse, o_ref, lse_ref, str(case))
+    check_bf16(o, lse, o_ref, lse_ref, str(case), out_quant=amp > 1.0)
 
 
 @pytest.mark.parametrize("cfg", [W.C2N, W.C2C], ids=lambda c: c.name)

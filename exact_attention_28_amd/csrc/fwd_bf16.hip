@@ -46,23 +46,37 @@ namespace xattn {
 // Word 3 of a gfx9 buffer resource for raw (unformatted, stride 0) 32-bit access.
 constexpr int kBufferWord3 = 0x00020000;
 
-template <int D, int HPW, bool CAUSAL, bool ROPE>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i mod 4) of the 8-byte chunks addressed by lanes i/4 + 4e, e = 0..3.  When
+// lane L of a group addresses row r0 + L/4, columns c0 + 4(L mod 4) .. +3 of a
+// row-major bf16 tile, lane i receives rows r0 .. r0+3 of column c0 + i.
+__device__ __forceinline__ s16x4 lds_read_tr16(const u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) char*)(p));
+}
+
+template <int D, int HPW, bool CAUSAL, bool ROPE, int NQB>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Skv,
     float scale_log2, const double2* __restrict__ tab, int n_qt, int n_bh) {
-  constexpr int BM = 128, BN = 64, NP = BM / HPW;
-  constexpr int KST = D + 8;                 // K row stride in LDS (elements)
-  constexpr int VST = BN + 8;                // V^T row stride in LDS (elements)
+  constexpr int BM = 128 * NQB, BN = 64, NP = BM / HPW;
+  // LDS row strides (elements), chosen so the fragment reads are free of bank
+  // conflicts: K rows are read 16 at a time with 16-byte reads (stride = 4 banks
+  // mod 64), V rows 4 at a time with 8-byte transpose reads (stride = 8 banks).
+  constexpr int KST = D + 8;
+  constexpr int VST = (D == 64) ? D + 8 : D + 16;
   constexpr int KCH = D / 8;                 // 16-byte chunks per row
-  constexpr int K_LD = BN * KCH / 256;       // K chunks per thread per tile
-  constexpr int V_LD = (BN / 2) * KCH / 256; // V (row pair, chunk) items per thread
+  constexpr int LD = BN * KCH / 256;         // 16-byte chunks per thread per tile (K and V each)
   constexpr int NDB = D / 32;                // 32-row blocks of O^T
   constexpr int NKS = D / 16;                // k-steps of the QK^T contraction
-  static_assert(K_LD >= 1 && V_LD >= 1, "tile loads");
+  static_assert(LD >= 1, "tile loads");
 
   __shared__ __attribute__((aligned(16))) u16 Ks[2][BN * KST];
-  __shared__ __attribute__((aligned(16))) u16 Vt[2][D * VST];
+  __shared__ __attribute__((aligned(16))) u16 Vs[2][BN * VST];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
@@ -77,21 +91,29 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   const int p0 = qt * NP;
   const int off = Skv - Sq;
 
-  const int gc = w * 32 + c;
-  const int hh = h0 + gc / NP;
-  const int pos = p0 + gc % NP;
-  const bool qvalid = pos < Sq;
+  // this lane's query columns: qb-th block of 32 columns of wave w
+  int hh[NQB], pos[NQB];
+  bool qvalid[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int gc = (w * NQB + qb) * 32 + c;
+    hh[qb] = h0 + gc / NP;
+    pos[qb] = p0 + gc % NP;
+    qvalid[qb] = pos[qb] < Sq;
+  }
 
-  // ---- query fragment: lane holds q[pos, hh, 16ks + 8g .. +7] for every ks
-  bf16x8 qf[NKS];
-  {
-    const u16* qp = Q + (((long long)b * Sq + (qvalid ? pos : 0)) * Hq + hh) * D + g * 8;
+  // ---- query fragments: lane holds q[pos, hh, 16ks + 8g .. +7] for every ks
+  bf16x8 qf[NQB][NKS];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const u16* qp =
+        Q + (((long long)b * Sq + (qvalid[qb] ? pos[qb] : 0)) * Hq + hh[qb]) * D + g * 8;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       u32x4 wv = {0u, 0u, 0u, 0u};
-      if (qvalid) wv = *reinterpret_cast<const u32x4*>(qp + ks * 16);
-      if (ROPE && qvalid) {
-        const double2* tp = tab + (long long)(off + pos) * (D / 2) + ks * 8 + g * 4;
+      if (qvalid[qb]) wv = *reinterpret_cast<const u32x4*>(qp + ks * 16);
+      if (ROPE && qvalid[qb]) {
+        const double2* tp = tab + (long long)(off + pos[qb]) * (D / 2) + ks * 8 + g * 4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           double r0, r1;
@@ -99,7 +121,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
           wv[e] = f64_to_bf16_bits(r0) | (f64_to_bf16_bits(r1) << 16);
         }
       }
-      qf[ks] = __builtin_bit_cast(bf16x8, wv);
+      qf[qb][ks] = __builtin_bit_cast(bf16x8, wv);
     }
   }
 
@@ -118,60 +140,55 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
       __builtin_amdgcn_make_buffer_rsrc((void*)(V + head_base), (short)0, nbytes, kBufferWord3);
   const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
 
-  uint32_t koff[K_LD], voff[V_LD];
+  uint32_t goff[LD];
+  int lrow[LD], lch[LD];
 #pragma unroll
-  for (int i = 0; i < K_LD; ++i) {
+  for (int i = 0; i < LD; ++i) {
     const int cid = tid + 256 * i;
-    koff[i] = (uint32_t)(cid / KCH) * row_bytes + (uint32_t)(cid % KCH) * 16u;
-  }
-#pragma unroll
-  for (int i = 0; i < V_LD; ++i) {
-    const int cid = tid + 256 * i;
-    voff[i] = (uint32_t)(2 * (cid / KCH)) * row_bytes + (uint32_t)(cid % KCH) * 16u;
+    lrow[i] = cid / KCH;
+    lch[i] = cid % KCH;
+    goff[i] = (uint32_t)lrow[i] * row_bytes + (uint32_t)lch[i] * 16u;
   }
 
-  u32x4 kreg[K_LD], vreg[2 * V_LD];
+  u32x4 kreg[LD], vreg[LD];
   auto gload = [&](int k0) {
     const uint32_t t0 = (uint32_t)k0 * row_bytes;
 #pragma unroll
-    for (int i = 0; i < K_LD; ++i)
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[i] + t0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < V_LD; ++i) {
-      vreg[2 * i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i] + t0, 0, 0);
-      vreg[2 * i + 1] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i] + t0 + row_bytes, 0, 0);
+    for (int i = 0; i < LD; ++i) {
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, goff[i] + t0, 0, 0);
+      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, goff[i] + t0, 0, 0);
     }
   };
   auto swrite = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < K_LD; ++i) {
-      const int cid = tid + 256 * i, row = cid / KCH, ch = cid % KCH;
-      *reinterpret_cast<u32x4*>(&Ks[buf][row * KST + ch * 8]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V_LD; ++i) {
-      const int cid = tid + 256 * i, pr = cid / KCH, ch = cid % KCH;
-      const u32x4 a = vreg[2 * i], bb = vreg[2 * i + 1];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // element e of row 2pr (low half) and of row 2pr+1 (high half)
-        const uint32_t word = __builtin_amdgcn_perm(bb[e >> 1], a[e >> 1],
-                                                    (e & 1) ? 0x07060302u : 0x05040100u);
-        *reinterpret_cast<uint32_t*>(&Vt[buf][(ch * 8 + e) * VST + 2 * pr]) = word;
-      }
+    for (int i = 0; i < LD; ++i) {
+      *reinterpret_cast<u32x4*>(&Ks[buf][lrow[i] * KST + lch[i] * 8]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&Vs[buf][lrow[i] * VST + lch[i] * 8]) = vreg[i];
     }
   };
 
-  f32x16 oacc[NDB];
+  // transpose-read addressing of the V^T fragments (see lds_read_tr16)
+  const int tq = lane >> 4, tl = lane & 15;
+  const int v_row0 = 4 * (tq >> 1) + (tl >> 2);         // + 16 kc + 8 r
+  const int v_col0 = 16 * (tq & 1) + 4 * (tl & 3);      // + 32 db
+
+  f32x16 oacc[NQB][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
   // m_run is a reference maximum (log2 domain): the true running maximum never
   // exceeds it by more than 8, so every probability stays <= 2^8; it is moved
   // (and O, l rescaled) only when a score would break that bound.  O / l and
   // m_run + log2(l) do not depend on which reference is used.
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run[NQB], l_run[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
 
   if (ntiles > 0) {
     gload(0);
@@ -188,129 +205,155 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     const int k0 = t * BN;
     if (t + 1 < ntiles) gload(k0 + BN);
 
-    // S^T (64 keys x 32 queries) = K_tile Q^T
-    f32x16 s[2];
+    // S^T (64 keys x 32 queries per block) = K_tile Q^T
+    f32x16 s[NQB][2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[0][r] = s[1][r] = 0.f;
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qb][0][r] = s[qb][1][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         const bf16x8 ka =
             *reinterpret_cast<const bf16x8*>(&Ks[buf][(blk * 32 + c) * KST + ks * 16 + g * 8]);
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[blk], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          s[qb][blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], s[qb][blk], 0, 0, 0);
       }
     }
 
     // mask: key rows past Skv, and keys after the query under the causal rule
     const bool need_mask = (k0 + BN > Skv) || (CAUSAL && k0 + BN - 1 > first_q);
     if (need_mask) {
-      const int qlim = CAUSAL ? min(pos + off, Skv - 1) : Skv - 1;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int qlim = CAUSAL ? min(pos[qb] + off, Skv - 1) : Skv - 1;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = k0 + blk * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (j > qlim) s[qb][blk][r] = -INFINITY;
+          }
+      }
+    }
+
+    // online softmax for this lane's query columns
+    bf16x8 pf[NQB][4];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
+#pragma unroll
+      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[qb][0][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][1][r]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const float mxs = mx * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(mxs > m_run[qb] + 8.f)) {  // wave-uniform
+        const float m_new = fmaxf(m_run[qb], mxs);
+        const float alpha =
+            __builtin_amdgcn_exp2f(m_run[qb] - (m_new == -INFINITY ? 0.f : m_new));
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+        m_run[qb] = m_new;
+      }
+      const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+      float ls = 0.f;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = k0 + blk * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (j > qlim) s[blk][r] = -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][blk][r], scale_log2, -m_use));
+          s[qb][blk][r] = p;
+          ls += p;
         }
+      l_run[qb] += ls;  // per half-wave partial; the halves are added after the loop
+      // probabilities as bf16 B operands: chunk kc covers keys 16kc .. 16kc+15
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[qb][kc][e] = (__bf16)s[qb][kc >> 1][(kc & 1) * 8 + e];
     }
 
-    // online softmax for this lane's query column
-    float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mxs = mx * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(mxs > m_run + 8.f)) {  // wave-uniform
-      const float m_new = fmaxf(m_run, mxs);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float ls = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[blk][r], scale_log2, -m_use));
-        s[blk][r] = p;
-        ls += p;
-      }
-    l_run += ls;  // per half-wave partial; the halves are added after the loop
-
-    // probabilities as bf16 B operands: chunk kc covers keys 16kc .. 16kc+15
-    bf16x8 pf[4];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[kc][e] = (__bf16)s[kc >> 1][(kc & 1) * 8 + e];
-
-    // O^T (D x 32) += V^T (D x 64) P^T (64 x 32)
+    // O^T (D x 32) += V^T (D x 64) P^T (64 x 32); V^T fragments by transpose reads
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const u16* vrow = &Vt[buf][(db * 32 + c) * VST + 4 * g];
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kc * 16);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kc * 16 + 8);
-        const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[kc],
-                                                           oacc[db], 0, 0, 0);
+        const u16* vp = &Vs[buf][(v_row0 + 16 * kc) * VST + v_col0 + 32 * db];
+        const s16x4 lo = lds_read_tr16(vp);
+        const s16x4 hi = lds_read_tr16(vp + 8 * VST);
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][kc], oacc[qb][db], 0, 0, 0);
       }
     }
 
     if (t + 1 < ntiles) swrite(buf ^ 1);
     __syncthreads();
   }
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
-                                                     __float_as_uint(l_run), false, false);
-    l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  }
 
-  if (qvalid) {
-    const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-    u16* op = O + (((long long)b * Sq + pos) * Hq + hh) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int qb = 0; qb < NQB; ++qb) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[qb]),
+                                                     __float_as_uint(l_run[qb]), false, false);
+    const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (qvalid[qb]) {
+      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+      u16* op = O + (((long long)b * Sq + pos[qb]) * Hq + hh[qb]) * D;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d = db * 32 + 8 * a + 4 * g;
-        u32x2 pk;
-        pk[0] = pack_bf16(oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv);
-        pk[1] = pack_bf16(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + d) = pk;
-      }
-    if (LSE != nullptr && g == 0)
-      LSE[((long long)b * Hq + hh) * Sq + pos] =
-          (l_run > 0.f) ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int d = db * 32 + 8 * a + 4 * g;
+          u32x2 pk;
+          pk[0] = pack_bf16(oacc[qb][db][4 * a] * inv, oacc[qb][db][4 * a + 1] * inv);
+          pk[1] = pack_bf16(oacc[qb][db][4 * a + 2] * inv, oacc[qb][db][4 * a + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + d) = pk;
+        }
+      if (LSE != nullptr && g == 0)
+        LSE[((long long)b * Hq + hh[qb]) * Sq + pos[qb]] =
+            (l_tot > 0.f) ? (m_run[qb] + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
   }
 }
 
-template <int D, int HPW, bool CAUSAL, bool ROPE>
+template <int D, int HPW, bool CAUSAL, bool ROPE, int NQB>
 static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int Hq, int Hkv, int Sq, int Skv, float scale, const double2* tab,
                           hipStream_t stream) {
-  constexpr int NP = 128 / HPW;
+  constexpr int NP = 128 * NQB / HPW;
   const int n_qt = (Sq + NP - 1) / NP;
   const int n_bh = B * (Hq / HPW);
   const long long nblocks = (long long)n_qt * n_bh;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  fwd_bf16_kernel<D, HPW, CAUSAL, ROPE><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
+  fwd_bf16_kernel<D, HPW, CAUSAL, ROPE, NQB><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
       static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v),
       static_cast<u16*>(o), lse, Hq, Hkv, Sq, Skv, scale * kLog2e, tab, n_qt, n_bh);
   return hipGetLastError();
+}
+
+// Two query blocks per wave halve the LDS traffic per MFMA; one block keeps
+// small problems spread over more workgroups (at least two per CU).
+template <int D, int HPW, bool CAUSAL, bool ROPE>
+static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                          int Hq, int Hkv, int Sq, int Skv, float scale, const double2* tab,
+                          hipStream_t stream) {
+  const long long wg2 = (long long)((Sq + 256 / HPW - 1) / (256 / HPW)) * B * (Hq / HPW);
+  if (wg2 >= 2 * 256)
+    return go_bf16<D, HPW, CAUSAL, ROPE, 2>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab,
+                                            stream);
+  return go_bf16<D, HPW, CAUSAL, ROPE, 1>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab,
+                                          stream);
 }
 
 template <int D, bool CAUSAL, bool ROPE>

@@ -38,6 +38,7 @@
 //    (batch, head group) index is the fastest-varying part of the block index
 //    so that the workgroups of one head group land on one XCD (block i runs on
 //    XCD i mod 8) and share its L2.
+
 #include "common.h"
 #include "kernels.h"
 
@@ -58,25 +59,59 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const u16* p) {
       (lds_s16x4*)(__attribute__((address_space(3))) char*)(p));
 }
 
+// s_waitcnt with vmcnt(0) and the other counters unconstrained.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(u16* p) {
+  return (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) char*)(p));
+}
+
+// Chunk swizzles (16-byte chunks, XORed with a function of the row).  LDS has
+// 64 four-byte banks, i.e. 16 groups of one chunk.  K fragments are read 16 rows
+// at a time at one logical chunk: the 16 (row, chunk) must fall in 16 distinct
+// groups.  V fragments are read by transpose reads covering 4 consecutive rows
+// (a multiple of 4 first) x 2 adjacent chunks (an even first): 8 distinct groups.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  return (D == 64) ? ((row >> 1) & 7) : (row & 15);  // group = (row*KCH + chunk) mod 16
+}
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  return (D == 64) ? (2 * ((row >> 1) & 3)) : (2 * (row & 3));
+}
+
+// Direct HBM->LDS loads of one wave's share of a K and a V tile: instruction i
+// fills the 64 consecutive 16-byte slots starting at kdst/vdst + 1 KiB * i.
+// (A plain device function: the gfx950 LDS-load builtin cannot sit in a lambda,
+// which is also compiled for the host.)
+template <int LD>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                         u16* kdst, u16* vdst, const uint32_t* koff,
+                                         const uint32_t* voff, uint32_t t0) {
+#pragma unroll
+  for (int i = 0; i < LD; ++i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_ptr(kdst + i * 64 * 8), 16, koff[i] + t0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_ptr(vdst + i * 64 * 8), 16, voff[i] + t0, 0, 0, 0);
+  }
+}
+
 template <int D, int HPW, bool CAUSAL, bool ROPE, int NQB>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Skv,
     float scale_log2, const double2* __restrict__ tab, int n_qt, int n_bh) {
   constexpr int BM = 128 * NQB, BN = 64, NP = BM / HPW;
-  // LDS row strides (elements), chosen so the fragment reads are free of bank
-  // conflicts: K rows are read 16 at a time with 16-byte reads (stride = 4 banks
-  // mod 64), V rows 4 at a time with 8-byte transpose reads (stride = 8 banks).
-  constexpr int KST = D + 8;
-  constexpr int VST = (D == 64) ? D + 8 : D + 16;
   constexpr int KCH = D / 8;                 // 16-byte chunks per row
   constexpr int LD = BN * KCH / 256;         // 16-byte chunks per thread per tile (K and V each)
   constexpr int NDB = D / 32;                // 32-row blocks of O^T
   constexpr int NKS = D / 16;                // k-steps of the QK^T contraction
   static_assert(LD >= 1, "tile loads");
 
-  __shared__ __attribute__((aligned(16))) u16 Ks[2][BN * KST];
-  __shared__ __attribute__((aligned(16))) u16 Vs[2][BN * VST];
+  // K and V tiles live in LDS unpadded (row = D bf16), written by direct
+  // HBM->LDS loads; 16-byte chunks are XOR-swizzled per row so the fragment
+  // reads hit distinct banks (see kswz / vswz).
+  __shared__ __attribute__((aligned(16))) u16 Ks[2][BN * D];
+  __shared__ __attribute__((aligned(16))) u16 Vs[2][BN * D];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
@@ -140,37 +175,44 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
       __builtin_amdgcn_make_buffer_rsrc((void*)(V + head_base), (short)0, nbytes, kBufferWord3);
   const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
 
-  uint32_t goff[LD];
-  int lrow[LD], lch[LD];
+  // A direct load writes lane l's 16 bytes to LDS base + 16 l, so slot
+  // s = (w*LD + i)*64 + lane of a tile is filled by this lane: it fetches the
+  // logical chunk that the swizzle places at (row s / KCH, chunk s % KCH).
+  uint32_t koff[LD], voff[LD];
 #pragma unroll
   for (int i = 0; i < LD; ++i) {
-    const int cid = tid + 256 * i;
-    lrow[i] = cid / KCH;
-    lch[i] = cid % KCH;
-    goff[i] = (uint32_t)lrow[i] * row_bytes + (uint32_t)lch[i] * 16u;
+    const int sl = (w * LD + i) * 64 + lane, row = sl / KCH, phys = sl % KCH;
+    koff[i] = (uint32_t)row * row_bytes + (uint32_t)(phys ^ kswz<D>(row)) * 16u;
+    voff[i] = (uint32_t)row * row_bytes + (uint32_t)(phys ^ vswz<D>(row)) * 16u;
   }
-
-  u32x4 kreg[LD], vreg[LD];
-  auto gload = [&](int k0) {
-    const uint32_t t0 = (uint32_t)k0 * row_bytes;
-#pragma unroll
-    for (int i = 0; i < LD; ++i) {
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, goff[i] + t0, 0, 0);
-      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, goff[i] + t0, 0, 0);
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LD; ++i) {
-      *reinterpret_cast<u32x4*>(&Ks[buf][lrow[i] * KST + lch[i] * 8]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&Vs[buf][lrow[i] * VST + lch[i] * 8]) = vreg[i];
-    }
+  auto dma = [&](int k0, int buf) {
+    dma_tile<LD>(rk, rv, &Ks[buf][w * LD * 64 * 8], &Vs[buf][w * LD * 64 * 8], koff, voff,
+                 (uint32_t)k0 * row_bytes);
   };
 
-  // transpose-read addressing of the V^T fragments (see lds_read_tr16)
+  // fragment addressing (elements within a tile buffer)
+  int ka_off[2][NKS];  // K fragment of key block blk, k-step ks: row blk*32 + c, chunk 2ks + g
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int row = blk * 32 + c;
+      ka_off[blk][ks] = row * D + ((2 * ks + g) ^ kswz<D>(row)) * 8;
+    }
+  // V^T fragments by transpose reads: lane (group tq, index tl) addresses row
+  // 16kc + 8r + 4g + tl/4 and logical column 32db + 16(tq&1) + 4(tl&3)
   const int tq = lane >> 4, tl = lane & 15;
-  const int v_row0 = 4 * (tq >> 1) + (tl >> 2);         // + 16 kc + 8 r
-  const int v_col0 = 16 * (tq & 1) + 4 * (tl & 3);      // + 32 db
+  int va_off[NDB][4][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = 16 * kc + 8 * r + 4 * (tq >> 1) + (tl >> 2);
+        const int col = 32 * db + 16 * (tq & 1) + 4 * (tl & 3);
+        va_off[db][kc][r] = row * D + (((col >> 3) ^ vswz<D>(row)) << 3) + (col & 7);
+      }
 
   f32x16 oacc[NQB][NDB];
 #pragma unroll
@@ -190,20 +232,16 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     l_run[qb] = 0.f;
   }
 
-  if (ntiles > 0) {
-    gload(0);
-    swrite(0);
-  }
-  // Everything the prologue loaded (the query fragment included) has landed:
-  // without this the loop head inherits a pending query load from the path
-  // with no tile and waits for every in-flight prefetch at each iteration.
+  if (ntiles > 0) dma(0, 0);
+  // everything the prologue loaded (query fragments, first tile) has landed
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int k0 = t * BN;
-    if (t + 1 < ntiles) gload(k0 + BN);
+    // the other buffer was last read in iteration t-1, which every wave has left
+    if (t + 1 < ntiles) dma(k0 + BN, buf ^ 1);
 
     // S^T (64 keys x 32 queries per block) = K_tile Q^T
     f32x16 s[NQB][2];
@@ -215,8 +253,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(&Ks[buf][(blk * 32 + c) * KST + ks * 16 + g * 8]);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][ka_off[blk][ks]]);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
           s[qb][blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], s[qb][blk], 0, 0, 0);
@@ -286,9 +323,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const u16* vp = &Vs[buf][(v_row0 + 16 * kc) * VST + v_col0 + 32 * db];
-        const s16x4 lo = lds_read_tr16(vp);
-        const s16x4 hi = lds_read_tr16(vp + 8 * VST);
+        const s16x4 lo = lds_read_tr16(&Vs[buf][va_off[db][kc][0]]);
+        const s16x4 hi = lds_read_tr16(&Vs[buf][va_off[db][kc][1]]);
         const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
         const u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
         const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
@@ -298,7 +334,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
       }
     }
 
-    if (t + 1 < ntiles) swrite(buf ^ 1);
+    // the next tile's direct loads have landed and every wave is done with this one
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
 
@@ -342,14 +379,15 @@ static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, 
   return hipGetLastError();
 }
 
-// Two query blocks per wave halve the LDS traffic per MFMA; one block keeps
-// small problems spread over more workgroups (at least two per CU).
+// Two query blocks per wave halve the LDS traffic per MFMA (D = 64, where the
+// registers allow it); one block keeps small problems spread over more
+// workgroups (at least two per CU).
 template <int D, int HPW, bool CAUSAL, bool ROPE>
 static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int Hq, int Hkv, int Sq, int Skv, float scale, const double2* tab,
                           hipStream_t stream) {
   const long long wg2 = (long long)((Sq + 256 / HPW - 1) / (256 / HPW)) * B * (Hq / HPW);
-  if (wg2 >= 2 * 256)
+  if (D == 64 && wg2 >= 2 * 256)
     return go_bf16<D, HPW, CAUSAL, ROPE, 2>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab,
                                             stream);
   return go_bf16<D, HPW, CAUSAL, ROPE, 1>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab,

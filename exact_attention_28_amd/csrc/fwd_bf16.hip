@@ -110,8 +110,14 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   // K and V tiles live in LDS unpadded (row = D bf16), written by direct
   // HBM->LDS loads; 16-byte chunks are XOR-swizzled per row so the fragment
   // reads hit distinct banks (see kswz / vswz).
-  __shared__ __attribute__((aligned(16))) u16 Ks[2][BN * D];
-  __shared__ __attribute__((aligned(16))) u16 Vs[2][BN * D];
+  // two buffers as separate arrays: with the loop unrolled by two, every LDS
+  // read and every direct load names its buffer statically, so the compiler
+  // can see that the tile being read is not the one being loaded (otherwise it
+  // waits for the in-flight load before each read)
+  __shared__ __attribute__((aligned(16))) u16 Ks0[BN * D];
+  __shared__ __attribute__((aligned(16))) u16 Vs0[BN * D];
+  __shared__ __attribute__((aligned(16))) u16 Ks1[BN * D];
+  __shared__ __attribute__((aligned(16))) u16 Vs1[BN * D];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
@@ -185,8 +191,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     koff[i] = (uint32_t)row * row_bytes + (uint32_t)(phys ^ kswz<D>(row)) * 16u;
     voff[i] = (uint32_t)row * row_bytes + (uint32_t)(phys ^ vswz<D>(row)) * 16u;
   }
-  auto dma = [&](int k0, int buf) {
-    dma_tile<LD>(rk, rv, &Ks[buf][w * LD * 64 * 8], &Vs[buf][w * LD * 64 * 8], koff, voff,
+  auto dma = [&](int k0, u16* kb, u16* vb) {
+    dma_tile<LD>(rk, rv, kb + w * LD * 64 * 8, vb + w * LD * 64 * 8, koff, voff,
                  (uint32_t)k0 * row_bytes);
   };
 
@@ -232,16 +238,16 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     l_run[qb] = 0.f;
   }
 
-  if (ntiles > 0) dma(0, 0);
+  if (ntiles > 0) dma(0, Ks0, Vs0);
   // everything the prologue loaded (query fragments, first tile) has landed
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  // one key/value tile: its K and V are in (kc_, vc_); the next tile is loaded
+  // into (kn_, vn_), last read in the previous step, which every wave has left
+  auto tile = [&](int t, const u16* kc_, const u16* vc_, u16* kn_, u16* vn_) {
     const int k0 = t * BN;
-    // the other buffer was last read in iteration t-1, which every wave has left
-    if (t + 1 < ntiles) dma(k0 + BN, buf ^ 1);
+    if (t + 1 < ntiles) dma(k0 + BN, kn_, vn_);
 
     // S^T (64 keys x 32 queries per block) = K_tile Q^T
     f32x16 s[NQB][2];
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][ka_off[blk][ks]]);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kc_[ka_off[blk][ks]]);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
           s[qb][blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], s[qb][blk], 0, 0, 0);
@@ -323,8 +329,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const s16x4 lo = lds_read_tr16(&Vs[buf][va_off[db][kc][0]]);
-        const s16x4 hi = lds_read_tr16(&Vs[buf][va_off[db][kc][1]]);
+        const s16x4 lo = lds_read_tr16(&vc_[va_off[db][kc][0]]);
+        const s16x4 hi = lds_read_tr16(&vc_[va_off[db][kc][1]]);
         const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
         const u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
         const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
@@ -337,6 +343,10 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     // the next tile's direct loads have landed and every wave is done with this one
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, Ks0, Vs0, Ks1, Vs1);
+    if (t + 1 < ntiles) tile(t + 1, Ks1, Vs1, Ks0, Vs0);
   }
 
 #pragma unroll

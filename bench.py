@@ -82,36 +82,116 @@ def timed(fn, reps, stream):
 
 
 def cpu_baseline(prefill, dec_inputs, budget_s):
-    """The fp64 oracle as it stands, timed on this host on a bounded sample."""
+    """The fp64 oracle as it stands, timed on this host on a bounded sample:
+    prefill (batch, head) units in rounds of one per thread until two thirds of
+    the budget are spent (or the workload is done), then whole passes of the
+    decode workload for the last third (at least one pass)."""
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     cfg = W.C4
     q, k, v = prefill
-    units = list(range(threads))  # one (batch, head) per thread: whole 4096x4096 score matrix
+    n_units = cfg.B * cfg.Hq
+    done = 0
     t0 = time.perf_counter()
-    oracle.attn_fwd(q, k, v, causal=True, scale=cfg.scale, rope_base=cfg.rope_base,
-                    units=units, nthreads=threads)
+    while done < n_units and (done == 0 or time.perf_counter() - t0 < budget_s * 2 / 3):
+        # one (batch, head) per thread: the whole 4096 x 4096 score matrix each
+        units = list(range(done, min(done + threads, n_units)))
+        oracle.attn_fwd(q, k, v, causal=True, scale=cfg.scale, rope_base=cfg.rope_base,
+                        units=units, nthreads=threads)
+        done += len(units)
     t_pre = time.perf_counter() - t0
-    flops = cfg.flops / (cfg.B * cfg.Hq) * len(units)
+    flops = cfg.flops / n_units * done
     out = {"value": flops / t_pre / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-           "sample": f"LFM2 GQA prefill, {len(units)} of {cfg.B * cfg.Hq} (batch, head) units "
+           "sample": f"LFM2 GQA prefill, {done} of {n_units} (batch, head) units "
                      f"(all 4096 query rows each), {t_pre:.1f} s"}
     qd, kc, vc, sl = dec_inputs
     dcfg = W.C5
-    n = 0
+    all_units = list(range(dcfg.B * dcfg.Hq))
+    # each unit reads its kv head's L_b rows of K and V once
+    pass_bytes = sum(int(sl[u // dcfg.Hq]) * dcfg.D * 2 * 2 for u in all_units)
+    passes = 0
     t0 = time.perf_counter()
-    kv_bytes = 0
-    while n < dcfg.B * dcfg.Hq and time.perf_counter() - t0 < budget_s / 3:
-        units = list(range(n, min(n + threads, dcfg.B * dcfg.Hq)))
-        oracle.decode(qd, kc, vc, sl, scale=dcfg.scale, units=units, nthreads=threads)
-        # each unit reads its kv head's L_b rows of K and V once
-        kv_bytes += sum(int(sl[u // dcfg.Hq]) * dcfg.D * 2 * 2 for u in units)
-        n += len(units)
+    while passes == 0 or time.perf_counter() - t0 < budget_s / 3:
+        oracle.decode(qd, kc, vc, sl, scale=dcfg.scale, units=all_units, nthreads=threads)
+        passes += 1
     t_dec = time.perf_counter() - t0
-    out["decode"] = {"value": kv_bytes / t_dec / 1e9, "unit": "GB/s",
-                     "sample": f"split-KV decode, {n} of {dcfg.B * dcfg.Hq} (batch, head) "
-                               f"units, {t_dec:.1f} s"}
+    out["decode"] = {"value": pass_bytes * passes / t_dec / 1e9, "unit": "GB/s",
+                     "sample": f"split-KV decode, {passes} pass(es) over all "
+                               f"{len(all_units)} (batch, head) units, {t_dec:.1f} s"}
     return out
+
+
+COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
+
+
+def profile_kernel(reps):
+    """For counter runs: `reps` launches of the prefill kernel alone (Q and K
+    rotated beforehand) on the LFM2 prefill workload, then `reps` launches of a
+    plain elementwise copy of COPY_BYTES (dst = src + 0) for calibration."""
+    pc = W.C4
+    q_np, k_np, v_np = W.prefill_inputs(pc)
+    q, k, v = W.to_device(q_np), W.to_device(k_np), W.to_device(v_np)
+    xa.rope_apply(q, 0, pc.rope_base)
+    xa.rope_apply(k, 0, pc.rope_base)
+    o = torch.empty_like(q)
+    lse = torch.empty((pc.B, pc.Hq, pc.Sq), dtype=torch.float32, device="cuda")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        xa.attn_fwd(q, k, v, causal=True, scale=pc.scale, o=o, lse=lse)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+    log("profile-kernel done")
+
+
+def traffic_summary(fetch_csv, write_csv, out_path, cmds):
+    """Writes the traffic summary read by read_traffic() from two rocprofv3
+    counter_collection CSVs (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch).
+    Each counter is scaled by expected / measured for the calibration copy."""
+    import csv
+
+    def per_dispatch(path, counter):
+        vals = {"attn": [], "copy": []}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            is_copy = "elementwise" in name and "add" in name.lower()  # not the fill of src
+            key = "attn" if "fwd_bf16_kernel" in name else ("copy" if is_copy else None)
+            if key:
+                vals[key].append(float(r["Counter_Value"]))
+        return {k_: float(np.mean(v_)) for k_, v_ in vals.items() if v_}
+
+    fe, wr = per_dispatch(fetch_csv, "FETCH_SIZE"), per_dispatch(write_csv, "WRITE_SIZE")
+    exp_kib = COPY_BYTES / 1024
+    f_fac, w_fac = exp_kib / fe["copy"], exp_kib / wr["copy"]
+    fetch_b, write_b = fe["attn"] * f_fac * 1024, wr["attn"] * w_fac * 1024
+    pc = W.C4
+    lines = [
+        "# HBM traffic of the prefill kernel fwd_bf16_kernel<D=64,HPW=4,causal> on the LFM2",
+        "# prefill workload (B4 Hq32 Hkv8 S4096 D64 bf16, Q/K pre-rotated), per launch.",
+        "# Counters are KiB per dispatch; each is scaled by expected/measured for a plain",
+        f"# elementwise copy of {COPY_BYTES} bytes (read {COPY_BYTES}, write {COPY_BYTES}).",
+        "# Commands (from the repository root, TMPDIR=/tmp):",
+        *[f"#   {c}" for c in cmds],
+        f"kernel_source_sha256_16: {kernel_hash()}",
+        f"fetch_kib_per_launch_raw: {fe['attn']:.1f}",
+        f"write_kib_per_launch_raw: {wr['attn']:.1f}",
+        f"copy_fetch_kib_raw: {fe['copy']:.1f}",
+        f"copy_write_kib_raw: {wr['copy']:.1f}",
+        f"fetch_scale: {f_fac:.4f}",
+        f"write_scale: {w_fac:.4f}",
+        f"fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"write_bytes_per_launch: {write_b:.0f}",
+        f"algorithmic_bytes_per_launch: {pc.io_bytes}",
+        f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
+    ]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main():
@@ -120,14 +200,26 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--cpu-budget", type=float, default=24.0)
+    ap.add_argument("--profile-kernel", type=int, default=0, metavar="REPS",
+                    help="only launch the prefill kernel REPS times, then a calibration copy")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary from two rocprofv3 counter CSVs")
+    ap.add_argument("--traffic-cmd", action="append", default=[],
+                    help="command line recorded in the traffic summary (repeatable)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, TRAFFIC_FILE, args.traffic_cmd)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.profile_kernel:
+        profile_kernel(args.profile_kernel)
+        return
     stream = torch.cuda.current_stream()
 
     # ---- inputs, resident in HBM before anything is timed

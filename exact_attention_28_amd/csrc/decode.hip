@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 
   // Loads are never predicated: a token past `end` reads the last valid row
   // (finite data) and gets probability 0, so no NaN beyond the length is read.
-  auto load_step = [&](int base, u32x4* kr, u32x4* vr) {
+  auto load_step = [&](int base, u32x4* kr, u32x4* vr) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
       const int t = min(base + (w * kDecUnroll + u) * TPW + slot, end - 1);
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + t * tok_stride));
     }
   };
-  auto consume = [&](int base, const u32x4* kr, const u32x4* vr) {
+  auto consume = [&](int base, const u32x4* kr, const u32x4* vr) __attribute__((always_inline)) {
     float sc[kDecUnroll][GW];
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {

@@ -54,6 +54,9 @@ def _declare(lib):
     lib.oracle_flash_decode_head.restype = i
     lib.oracle_attn_tiled_head.argtypes = [_dp, _dp, _dp, i, i, i, i, d, i, i, _dp, _dp]
     lib.oracle_attn_tiled_head.restype = i
+    lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, d, d, i, _ip, i,
+                                    _dp, _dp, _dp, i]
+    lib.oracle_attn_bwd.restype = i
     lib.oracle_round_sig.argtypes = [d, i]
     lib.oracle_round_sig.restype = d
     return lib
@@ -130,6 +133,41 @@ def attn_fwd(q, k, v, causal=False, scale=None, rope_base=0.0, round_bits=None, 
     if rows is None and units is None:
         return o.reshape(B, Hq, Sq, D).transpose(0, 2, 1, 3).copy(), lse.reshape(B, Hq, Sq)
     return o, lse
+
+
+def attn_bwd(q, k, v, dout, causal=False, scale=None, rope_base=0.0, round_bits=None,
+             units=None, nthreads=1, lib=None):
+    """Gradients (dq [B,Sq,Hq,D], dk and dv [B,Skv,Hkv,D], fp64) of the
+    attention of attn_fwd for the upstream gradient dout [B,Sq,Hq,D].
+
+    units: list of b*Hkv + g (a kv head with its query heads) to evaluate;
+    None = all.  Slices of other units are returned as NaN."""
+    lib = lib or load()
+    q, dt = _as_input(q)
+    k, dtk = _as_input(k)
+    v, dtv = _as_input(v)
+    do, dtd = _as_input(dout)
+    assert dt == dtk == dtv == dtd, "q, k, v, dout must share a dtype"
+    B, Sq, Hq, D = q.shape
+    _, Skv, Hkv, _ = k.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D or do.shape != q.shape:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape} dout{do.shape}")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if round_bits is None:
+        round_bits = default_round_bits(dt)
+    units_a, nunits = _ints(units)
+    dq = np.full((B, Sq, Hq, D), np.nan)
+    dk = np.full((B, Skv, Hkv, D), np.nan)
+    dv = np.full((B, Skv, Hkv, D), np.nan)
+    st = lib.oracle_attn_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, do.ctypes.data, dt, B,
+                             Hq, Hkv, Sq, Skv, D, int(bool(causal)), float(scale),
+                             float(rope_base), int(round_bits),
+                             _ptr(units_a, _ip) if units_a is not None else None, nunits,
+                             _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads))
+    if st != 0:
+        raise ValueError(f"oracle_attn_bwd rejected its arguments (status {st})")
+    return dq, dk, dv
 
 
 def decode(q, kcache, vcache, seqlens, scale=None, units=None, nthreads=1, lib=None):

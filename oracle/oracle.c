@@ -347,6 +347,211 @@ int oracle_decode(const void* q, const void* kc, const void* vc, int dtype, cons
   return 0;
 }
 
+/* ------------------------------------------------------------ backward -- */
+
+/* Rotation by the negated angle, R(pos)^T: the gradient of the pre-rotation
+ * input from the gradient of the rotated one ([GQA] backward through grouped
+ * attention: un-rotate by applying RoPE with the sine negated). */
+static void rope_rotate_back(double* x, int D, double pos, double base) {
+  for (int i = 0; i < D / 2; ++i) {
+    const double theta = pos / pow(base, (2.0 * i) / (double)D);
+    const double c = cos(theta), sn = sin(theta);
+    const double x0 = x[2 * i], x1 = x[2 * i + 1];
+    x[2 * i] = x0 * c + x1 * sn;
+    x[2 * i + 1] = -x0 * sn + x1 * c;
+  }
+}
+
+typedef struct {
+  const void *q, *k, *v, *dout;
+  int dtype;
+  int B, Hq, Hkv, Sq, Skv, D, causal;
+  double scale, rope_base;
+  int round_bits;
+  const int* units; /* b*Hkv + g to evaluate (NULL: all) */
+  int nunits;
+  double *dq, *dk, *dv; /* [B,Sq,Hq,D], [B,Skv,Hkv,D], [B,Skv,Hkv,D] */
+  int nthreads, tid;
+  int status;
+} bwd_job;
+
+/* One (batch, kv head g) with all the query heads of its group: the gradient of
+ * O = softmax(S) V, S = scale Q~ K~^T (masked), written out from the full
+ * matrices ([FA] fn flash_backward_head gives the same quantities per block;
+ * [GQA] sums dK, dV over the query heads of a group):
+ *   P = softmax(S) by rows,  dV_g += P^T dO,  dP = dO V^T,
+ *   D_i = sum_j P_ij dP_ij  (= rowsum(dO o O) since O = P V),
+ *   dS = P o (dP - D),  dQ~ = scale dS K~,  dK~_g += scale dS^T Q~,
+ * then dQ = R^T dQ~ and dK = R^T dK~ when RoPE is on (R at the same positions
+ * as in the forward).  A row with no visible key has P = 0 and contributes
+ * nothing. */
+static int bwd_unit(const bwd_job* J, int unit) {
+  const int D = J->D, Skv = J->Skv, Sq = J->Sq, Hq = J->Hq, Hkv = J->Hkv;
+  const int b = unit / Hkv, g = unit % Hkv;
+  const int group = Hq / Hkv;
+  const int use_rope = J->rope_base > 0.0;
+  double* kt = (double*)malloc(sizeof(double) * (size_t)Skv * D);
+  double* vt = (double*)malloc(sizeof(double) * (size_t)Skv * D);
+  double* qt = (double*)malloc(sizeof(double) * (size_t)Sq * D);
+  double* dot_ = (double*)malloc(sizeof(double) * (size_t)Sq * D);
+  double* P = (double*)malloc(sizeof(double) * (size_t)Sq * Skv);
+  double* dP = (double*)malloc(sizeof(double) * (size_t)Sq * Skv);
+  double* dkt = (double*)calloc((size_t)Skv * D, sizeof(double));
+  double* dvt = (double*)calloc((size_t)Skv * D, sizeof(double));
+  double* dqt = (double*)malloc(sizeof(double) * (size_t)D);
+  if (!kt || !vt || !qt || !dot_ || !P || !dP || !dkt || !dvt || !dqt) {
+    free(kt); free(vt); free(qt); free(dot_); free(P); free(dP); free(dkt); free(dvt); free(dqt);
+    return -2;
+  }
+  for (int j = 0; j < Skv; ++j) {
+    const size_t base_idx = (((size_t)b * Skv + j) * Hkv + g) * D;
+    for (int d = 0; d < D; ++d) {
+      kt[(size_t)j * D + d] = widen(J->k, J->dtype, base_idx + d);
+      vt[(size_t)j * D + d] = widen(J->v, J->dtype, base_idx + d);
+    }
+    if (use_rope) {
+      rope_rotate(kt + (size_t)j * D, D, (double)j, J->rope_base);
+      for (int d = 0; d < D; ++d)
+        kt[(size_t)j * D + d] = oracle_round_sig(kt[(size_t)j * D + d], J->round_bits);
+    }
+  }
+#if MUT == 10
+  const int h_end = g * group + 1; /* planted: only the first query head of a group */
+#else
+  const int h_end = (g + 1) * group;
+#endif
+  for (int h = g * group; h < h_end; ++h) {
+    for (int i = 0; i < Sq; ++i) {
+      const size_t qbase = (((size_t)b * Sq + i) * Hq + h) * D;
+      for (int d = 0; d < D; ++d) {
+        qt[(size_t)i * D + d] = widen(J->q, J->dtype, qbase + d);
+        dot_[(size_t)i * D + d] = widen(J->dout, J->dtype, qbase + d);
+      }
+      if (use_rope) {
+        rope_rotate(qt + (size_t)i * D, D, (double)(Skv - Sq + i), J->rope_base);
+        for (int d = 0; d < D; ++d)
+          qt[(size_t)i * D + d] = oracle_round_sig(qt[(size_t)i * D + d], J->round_bits);
+      }
+    }
+    /* P by rows (masked entries exactly 0), and dP = dO V^T */
+    for (int i = 0; i < Sq; ++i) {
+      double* prow = P + (size_t)i * Skv;
+      double m = -INFINITY;
+      for (int j = 0; j < Skv; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += qt[(size_t)i * D + d] * kt[(size_t)j * D + d];
+        const int hidden = J->causal && j > i + (Skv - Sq);
+        prow[j] = hidden ? -INFINITY : J->scale * dot;
+        if (prow[j] > m) m = prow[j];
+      }
+      double l = 0.0;
+      for (int j = 0; j < Skv; ++j) {
+        prow[j] = (m == -INFINITY || prow[j] == -INFINITY) ? 0.0 : exp(prow[j] - m);
+        l += prow[j];
+      }
+      for (int j = 0; j < Skv; ++j) prow[j] = (l > 0.0) ? prow[j] / l : 0.0;
+      for (int j = 0; j < Skv; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += dot_[(size_t)i * D + d] * vt[(size_t)j * D + d];
+        dP[(size_t)i * Skv + j] = dot;
+      }
+    }
+    /* dV += P^T dO */
+    for (int j = 0; j < Skv; ++j)
+      for (int i = 0; i < Sq; ++i) {
+        const double pij = P[(size_t)i * Skv + j];
+        if (pij == 0.0) continue;
+        for (int d = 0; d < D; ++d) dvt[(size_t)j * D + d] += pij * dot_[(size_t)i * D + d];
+      }
+    /* dS = P o (dP - D) in place of dP; dQ~ = scale dS K~; dK~ += scale dS^T Q~ */
+    for (int i = 0; i < Sq; ++i) {
+      double Di = 0.0;
+      for (int j = 0; j < Skv; ++j) Di += P[(size_t)i * Skv + j] * dP[(size_t)i * Skv + j];
+      for (int j = 0; j < Skv; ++j) {
+#if MUT == 7
+        dP[(size_t)i * Skv + j] = P[(size_t)i * Skv + j] * dP[(size_t)i * Skv + j]; /* planted: D dropped */
+#else
+        dP[(size_t)i * Skv + j] = P[(size_t)i * Skv + j] * (dP[(size_t)i * Skv + j] - Di);
+#endif
+      }
+      for (int d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int j = 0; j < Skv; ++j) acc += dP[(size_t)i * Skv + j] * kt[(size_t)j * D + d];
+        dqt[d] = J->scale * acc;
+      }
+#if MUT != 9
+      if (use_rope) rope_rotate_back(dqt, D, (double)(Skv - Sq + i), J->rope_base);
+#endif
+      const size_t qbase = (((size_t)b * Sq + i) * Hq + h) * D;
+      for (int d = 0; d < D; ++d) J->dq[qbase + d] = dqt[d];
+    }
+    for (int j = 0; j < Skv; ++j)
+      for (int i = 0; i < Sq; ++i) {
+        const double ds = dP[(size_t)i * Skv + j];
+        if (ds == 0.0) continue;
+#if MUT == 8
+        const double sc = 1.0; /* planted: scale dropped from dK */
+#else
+        const double sc = J->scale;
+#endif
+        for (int d = 0; d < D; ++d) dkt[(size_t)j * D + d] += sc * ds * qt[(size_t)i * D + d];
+      }
+  }
+  for (int j = 0; j < Skv; ++j) {
+#if MUT != 9
+    if (use_rope) rope_rotate_back(dkt + (size_t)j * D, D, (double)j, J->rope_base);
+#endif
+    const size_t base_idx = (((size_t)b * Skv + j) * Hkv + g) * D;
+    for (int d = 0; d < D; ++d) {
+      J->dk[base_idx + d] = dkt[(size_t)j * D + d];
+      J->dv[base_idx + d] = dvt[(size_t)j * D + d];
+    }
+  }
+  free(kt); free(vt); free(qt); free(dot_); free(P); free(dP); free(dkt); free(dvt); free(dqt);
+  return 0;
+}
+
+static void* bwd_worker(void* arg) {
+  bwd_job* J = (bwd_job*)arg;
+  const int nunits = J->units ? J->nunits : J->B * J->Hkv;
+  for (int s = J->tid; s < nunits; s += J->nthreads) {
+    int st = bwd_unit(J, J->units ? J->units[s] : s);
+    if (st) { J->status = st; break; }
+  }
+  return NULL;
+}
+
+/* Gradients of the attention of oracle_attn_fwd with respect to q, k and v for
+ * an upstream gradient dout [B,Sq,Hq,D] (same dtype as q).  dq [B,Sq,Hq,D],
+ * dk and dv [B,Skv,Hkv,D] are fp64 arrays owned by the caller; the slices of
+ * the listed units (b*Hkv + g: a kv head with its query heads) are written,
+ * the rest is left untouched.  Units are spread over `nthreads` threads. */
+int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                    int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal, double scale,
+                    double rope_base, int round_bits, const int* units, int nunits,
+                    double* dq, double* dk, double* dv, int nthreads) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1) return -1;
+  if (Hq % Hkv != 0) return -1;
+  if (rope_base > 0.0 && D % 2 != 0) return -1;
+  if (nthreads < 1) nthreads = 1;
+  bwd_job* jobs = (bwd_job*)calloc((size_t)nthreads, sizeof(bwd_job));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  if (!jobs || !th) { free(jobs); free(th); return -2; }
+  for (int t = 0; t < nthreads; ++t) {
+    bwd_job j = {q, k, v, dout, dtype, B, Hq, Hkv, Sq, Skv, D, causal, scale, rope_base,
+                 round_bits, units, nunits, dq, dk, dv, nthreads, t, 0};
+    jobs[t] = j;
+  }
+  int status = 0;
+  for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, bwd_worker, &jobs[t]);
+  bwd_worker(&jobs[0]);
+  for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+  for (int t = 0; t < nthreads; ++t)
+    if (jobs[t].status) status = jobs[t].status;
+  free(jobs); free(th);
+  return status;
+}
+
 /* ------------------------------------------- algorithms of the pages -- */
 
 /* [FD] fn combine_tile_outputs: drop parts whose lse is not finite; none left

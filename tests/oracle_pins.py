@@ -434,4 +434,100 @@ def pin_sampled_rows(lib):
         np.testing.assert_array_equal(ls[ui], lse[b, h, rows])
 
 
+# ---------------------------------------------------------- backward --
+
+def _torch_rope(x, pos0, base):
+    """Differentiable pair rotation (the complex multiplication of _rope_complex)."""
+    B, S, H, D = x.shape
+    pos = pos0 + torch.arange(S, dtype=torch.float64)
+    inv = base ** (-2.0 * torch.arange(D // 2, dtype=torch.float64) / D)
+    ang = pos[:, None] * inv[None, :]
+    c, s = torch.cos(ang)[None, :, None, :], torch.sin(ang)[None, :, None, :]
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    return torch.stack((x0 * c - x1 * s, x0 * s + x1 * c), dim=-1).reshape(B, S, H, D)
+
+
+def _torch_grads(q, k, v, dout, causal, scale, rope_base):
+    """Reverse-mode gradients of sum(O * dout) from a plain fp64 torch attention
+    (GQA by repeating kv heads, bottom-right causal mask, RoPE as above)."""
+    q, k, v = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    qr = _torch_rope(q, Skv - Sq, rope_base) if rope_base > 0 else q
+    kr = _torch_rope(k, 0, rope_base) if rope_base > 0 else k
+    kh = kr.permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    vh = v.permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    s = scale * qr.permute(0, 2, 1, 3) @ kh.transpose(-1, -2)
+    if causal:
+        i = torch.arange(Sq)[:, None]
+        j = torch.arange(Skv)[None, :]
+        s = s.masked_fill(j > i + (Skv - Sq), float("-inf"))
+    o = (torch.softmax(s, dim=-1) @ vh).permute(0, 2, 1, 3)
+    (o * torch.tensor(dout, dtype=torch.float64)).sum().backward()
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+def pin_bwd_autograd(lib):
+    """Gradients equal reverse-mode differentiation of a plain torch fp64
+    attention: GQA groups, causal (square and Sq < Skv), RoPE, no mask."""
+    rng = np.random.default_rng(30)
+    for (B, Hq, Hkv, Sq, Skv, D, causal, rope) in ((1, 4, 2, 6, 6, 8, True, 100.0),
+                                                   (2, 2, 1, 3, 7, 8, True, 0.0),
+                                                   (1, 3, 3, 5, 4, 4, False, 50.0),
+                                                   (1, 6, 2, 4, 9, 6, True, 1000.0)):
+        q, k, v = _rand(rng, B, Sq, Hq, D), _rand(rng, B, Skv, Hkv, D), _rand(rng, B, Skv, Hkv, D)
+        do = _rand(rng, B, Sq, Hq, D)
+        got = oracle.attn_bwd(q, k, v, do, causal=causal, scale=0.4, rope_base=rope,
+                              round_bits=0, lib=lib)
+        ref = _torch_grads(q, k, v, do, causal, 0.4, rope)
+        for g, r in zip(got, ref):
+            np.testing.assert_allclose(g, r, atol=1e-11, rtol=0)
+
+
+def pin_bwd_finite_differences(lib):
+    """Central differences of L = sum(O * G) through the forward oracle."""
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, Sq, Skv, D = 1, 2, 1, 3, 4, 4
+    q, k, v = _rand(rng, B, Sq, Hq, D), _rand(rng, B, Skv, Hkv, D), _rand(rng, B, Skv, Hkv, D)
+    G = _rand(rng, B, Sq, Hq, D)
+    kw = dict(causal=True, scale=0.5, rope_base=30.0, round_bits=0, lib=lib)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, G, **kw)
+
+    def loss(q_, k_, v_):
+        return float((oracle.attn_fwd(q_, k_, v_, **kw)[0] * G).sum())
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": (q, k, v), "k": (q, k, v), "v": (q, k, v)}[name]
+            a_p = [xp if n == name else a for n, a in zip("qkv", args)]
+            a_m = [xm if n == name else a for n, a in zip("qkv", args)]
+            num[idx] = (loss(*a_p) - loss(*a_m)) / (2 * h)
+        np.testing.assert_allclose(g, num, atol=2e-8, rtol=0, err_msg=name)
+
+
+def pin_bwd_invariants(lib):
+    """Without RoPE the keys' gradients of a (batch, kv head) sum to zero
+    (softmax is unchanged by adding one vector to every key); each row of P
+    sums to one, so the values' gradients of a kv head sum to the summed dO of
+    its query heads (every row sees at least one key here); with a single key
+    P = 1, so dq = dk = 0 and dv = that sum."""
+    rng = np.random.default_rng(32)
+    B, Hq, Hkv, Sq, Skv, D = 2, 4, 2, 5, 7, 8
+    q, k, v = _rand(rng, B, Sq, Hq, D), _rand(rng, B, Skv, Hkv, D), _rand(rng, B, Skv, Hkv, D)
+    do = _rand(rng, B, Sq, Hq, D)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, causal=True, scale=0.3, round_bits=0, lib=lib)
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+    dsum = do.reshape(B, Sq, Hkv, Hq // Hkv, D).sum(axis=(1, 3))
+    np.testing.assert_allclose(dv.sum(axis=1), dsum, atol=1e-12)
+    k1, v1 = k[:, :1], v[:, :1]
+    dq, dk, dv = oracle.attn_bwd(q, k1, v1, do, causal=False, scale=0.3, round_bits=0, lib=lib)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-14)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-14)
+    np.testing.assert_allclose(dv[:, 0], dsum, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -3,7 +3,8 @@
 Each mutation is a compile-time switch in oracle.c (ORACLE_MUTATION=n) that
 introduces one plausible slip: interleaved instead of contiguous GQA groups,
 top-left instead of bottom-right causal alignment, RoPE rotating the wrong way,
-K used in place of V, the scale dropped, a base-2 log in the LSE.  The mutants
+K used in place of V, the scale dropped, a base-2 log in the LSE; in the
+backward, the D term, dK's scale, the inverse rotation, or the group sum.  The mutants
 are built into a temporary directory; the product oracle is untouched.
 """
 import os
@@ -21,6 +22,10 @@ MUTATIONS = {
     4: "K used as V",
     5: "scale dropped",
     6: "base-2 log in LSE",
+    7: "backward without the rowsum(dO o O) term",
+    8: "backward without the scale on dK",
+    9: "backward without the inverse rotation",
+    10: "backward dK/dV from one query head of a group",
 }
 
 

@@ -35,7 +35,7 @@ import workloads as W  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 METRIC = "attention fwd TFLOP/s + decode KV GB/s, as % of MI355X MFMA/HBM peak"
-KERNEL_SOURCES = ("fwd_bf16.hip", "common.h")
+KERNEL_SOURCES = ("fwd_bf16.hip", "common.h", "lds.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_lfm2_gqa_prefill_s4096_traffic.txt")
 
 

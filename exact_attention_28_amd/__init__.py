@@ -23,8 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_EMPTY_KV = 0, -1, -2, -3, -4
-EXPORTS = ("attn_fwd", "attn_decode_workspace_bytes", "attn_decode_splitkv", "rope_apply",
-           "attn_last_error")
+EXPORTS = ("attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_decode_workspace_bytes",
+           "attn_decode_splitkv", "rope_apply", "attn_last_error")
 
 _lib = None
 
@@ -46,6 +46,11 @@ def load():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, i, vp]
     lib.attn_fwd.restype = i
+    lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, f]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, i, vp,
+                             vp]
+    lib.attn_bwd.restype = i
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp]
@@ -114,6 +119,42 @@ def attn_fwd(q, k, v, causal=False, scale=None, rope_base=0.0, o=None, lse=None,
                            int(bool(causal)), float(scale), float(rope_base), _dtype_code(q),
                            _stream(stream)))
     return o, lse
+
+
+def attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, rope_base=0.0):
+    return int(load().attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, float(rope_base)))
+
+
+def attn_bwd(q, k, v, o, dout, lse, causal=False, scale=None, rope_base=0.0, dq=None, dk=None,
+             dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of attn_fwd for the upstream gradient dout.
+
+    q, k, v, causal, scale, rope_base as given to attn_fwd; o and lse its
+    outputs; dout like o.  Returns dq like q, dk and dv like k."""
+    _need_gpu(q, k, v, o, dout, lse, dq, dk, dv, workspace)
+    B, Sq, Hq, D = q.shape
+    Bk, Skv, Hkv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have q's shape")
+    if tuple(lse.shape) != (B, Hq, Sq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [B, Hq, Sq]")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
+        raise TypeError("q, k, v, o, dout must share a dtype")
+    if workspace is not None and workspace.numel() * workspace.element_size() < \
+            attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, rope_base):
+        raise ValueError("workspace smaller than attn_bwd_workspace_bytes")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                           _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
+                           float(scale), float(rope_base), _dtype_code(q), _ptr(workspace),
+                           _stream(stream)))
+    return dq, dk, dv
 
 
 def attn_decode_workspace_bytes(B, Hq, D, num_splits):

@@ -47,6 +47,8 @@ struct DevBuffers {
   size_t kstage_bytes = 0;
   void* dec_ws = nullptr;
   size_t dec_ws_bytes = 0;
+  void* bwd_ws = nullptr;
+  size_t bwd_ws_bytes = 0;
 };
 
 std::mutex g_mu;
@@ -149,6 +151,70 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     e = xattn::launch_fwd_f32(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab,
                               stream);
   return hip_status(e, "attn_fwd: kernel launch");
+}
+
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D, float rope_base) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1) return 0;
+  return xattn::bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, rope_base > 0.f);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+             int Skv, int D, int causal, float scale, float rope_base, int dtype,
+             void* workspace, hipStream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return fail(ATTN_ERR_INVALID, "attn_bwd: null q, k, v, o, dout, lse, dq, dk or dv");
+  if (Skv == 0) return fail(ATTN_ERR_EMPTY_KV, "attn_bwd: no keys (Skv == 0)");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1)
+    return fail(ATTN_ERR_INVALID, "attn_bwd: sizes must be >= 1 (B=%d Hq=%d Hkv=%d Sq=%d Skv=%d D=%d)",
+                B, Hq, Hkv, Sq, Skv, D);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_INVALID, "attn_bwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID, "attn_bwd: causal must be 0 or 1");
+  if (!finite_pos(scale)) return fail(ATTN_ERR_INVALID, "attn_bwd: scale must be finite and > 0");
+  if (std::isnan(rope_base) || std::isinf(rope_base))
+    return fail(ATTN_ERR_INVALID, "attn_bwd: rope_base must be finite");
+  const bool rope = rope_base > 0.f;
+  if (rope && D % 2 != 0) return fail(ATTN_ERR_INVALID, "attn_bwd: RoPE needs an even head dim");
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_INVALID, "attn_bwd: unknown dtype %d", dtype);
+  if (dtype != ATTN_BF16 || D != 64)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: built for bf16 with D=64 (dtype=%d D=%d)", dtype,
+                D);
+  if (rope && Sq > Skv)
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "attn_bwd: RoPE with Sq > Skv would place queries at negative positions");
+  // 32-bit buffer offsets within one batch; grid sizes
+  if ((long long)Sq * Hq * D * 2 >= 0x7fffffffLL || (long long)Skv * Hkv * D * 2 >= 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: one batch's Q or K exceeds 2 GiB");
+  if ((long long)B * Hq * ((Sq + 31) / 32) > 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: grid too large");
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  int st;
+  DevBuffers* db = buffers(&st);
+  if (!db) return st;
+  const double2* tab = nullptr;
+  if (rope) {
+    const size_t tab_bytes = (size_t)Skv * (D / 2) * sizeof(double2);
+    if ((st = grow(&db->rope_tab, &db->rope_tab_bytes, tab_bytes, "rope table")) != ATTN_OK)
+      return st;
+    tab = static_cast<const double2*>(db->rope_tab);
+    hipError_t e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), 0, Skv, D,
+                                            (double)rope_base, stream);
+    if (e != hipSuccess) return hip_status(e, "attn_bwd: rope table launch");
+  }
+  void* ws = workspace;
+  if (ws == nullptr) {
+    if ((st = grow(&db->bwd_ws, &db->bwd_ws_bytes,
+                   xattn::bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, rope), "backward workspace")) !=
+        ATTN_OK)
+      return st;
+    ws = db->bwd_ws;
+  }
+  hipError_t e = xattn::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D,
+                                        causal, scale, tab, ws, stream);
+  return hip_status(e, "attn_bwd: kernel launch");
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {

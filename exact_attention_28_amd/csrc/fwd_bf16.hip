@@ -41,30 +41,9 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "lds.h"
 
 namespace xattn {
-
-// Word 3 of a gfx9 buffer resource for raw (unformatted, stride 0) 32-bit access.
-constexpr int kBufferWord3 = 0x00020000;
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
-// (i mod 4) of the 8-byte chunks addressed by lanes i/4 + 4e, e = 0..3.  When
-// lane L of a group addresses row r0 + L/4, columns c0 + 4(L mod 4) .. +3 of a
-// row-major bf16 tile, lane i receives rows r0 .. r0+3 of column c0 + i.
-__device__ __forceinline__ s16x4 lds_read_tr16(const u16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(__attribute__((address_space(3))) char*)(p));
-}
-
-// s_waitcnt with vmcnt(0) and the other counters unconstrained.
-constexpr int kWaitVmcnt0 = 0x0F70;
-
-__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(u16* p) {
-  return (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) char*)(p));
-}
 
 // Chunk swizzles (16-byte chunks, XORed with a function of the row).  LDS has
 // 64 four-byte banks, i.e. 16 groups of one chunk.  K fragments are read 16 rows

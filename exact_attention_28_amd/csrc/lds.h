@@ -1,0 +1,43 @@
+// lds.h — buffer resources, direct HBM->LDS loads and LDS transpose reads on
+// gfx950, shared by the MFMA attention kernels.
+#pragma once
+
+#include "common.h"
+
+namespace xattn {
+
+// Word 3 of a gfx9 buffer resource for raw (unformatted, stride 0) 32-bit access.
+constexpr int kBufferWord3 = 0x00020000;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i mod 4) of the 8-byte chunks addressed by lanes i/4 + 4e, e = 0..3.  When
+// lane L of a group addresses row r0 + L/4, columns c0 + 4(L mod 4) .. +3 of a
+// row-major bf16 tile, lane i receives rows r0 .. r0+3 of column c0 + i.
+__device__ __forceinline__ s16x4 lds_read_tr16(const u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) char*)(p));
+}
+
+// s_waitcnt with vmcnt(0) and the other counters unconstrained.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(u16* p) {
+  return (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) char*)(p));
+}
+
+// Direct HBM->LDS loads: instruction i writes lane l's 16 bytes (buffer offset
+// off[i] + t0) to dst + 1 KiB * i + 16 l.  (A plain device function: the
+// gfx950 LDS-load builtin cannot sit in a lambda, which is also compiled for
+// the host.)
+template <int LD>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rsrc, u16* dst, const uint32_t* off,
+                                         uint32_t t0) {
+#pragma unroll
+  for (int i = 0; i < LD; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(dst + i * 64 * 8), 16, off[i] + t0, 0, 0, 0);
+}
+
+}  // namespace xattn

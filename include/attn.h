@@ -24,7 +24,7 @@
  *    enqueued and attn_last_error() describes the problem.  Nothing throws
  *    across the ABI.
  *  - Library-owned device buffers (RoPE tables, rotated-K staging, the default
- *    decode workspace) are allocated on first need, grow only, and are kept per
+ *    decode and backward workspaces) are allocated on first need, grow only, and are kept per
  *    device until the process ends; calls that use them concurrently on
  *    different streams of one device must be ordered by the caller.
  */
@@ -90,6 +90,51 @@ typedef enum {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
              int Hkv, int Sq, int Skv, int D, int causal, float scale, float rope_base,
              int dtype, hipStream_t stream);
+
+/*
+ * attn_bwd_workspace_bytes — size of the workspace attn_bwd needs: the per-row
+ * D_i and log2 lse ([B, Hq, Sq] fp32 each) and, with rope_base > 0, the rotated
+ * Q and K (B*Sq*Hq*D and B*Skv*Hkv*D bf16), each part rounded up to 256 bytes.
+ * Returns 0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D, float rope_base);
+
+/*
+ * attn_bwd — gradients of attn_fwd with respect to q, k and v.
+ *
+ * The FA-2 backward per head of [FA] fn flash_backward_head, with dK and dV
+ * summed over the query heads of each group and the gradients of the
+ * pre-rotation Q and K obtained by the inverse rotation ([GQA] backward through
+ * grouped attention).  With s_ij, g, q~, k~ as in attn_fwd and dO = dout:
+ *   P_ij  = exp(s_ij - lse[b,h,i])         (0 where masked, and for a row whose
+ *                                          lse is -inf)
+ *   D_i   = sum_d dO[b,i,h,d] O[b,i,h,d]
+ *   dS_ij = P_ij (<dO[b,i,h,:], v[b,j,g,:]> - D_i)
+ *   dv[b,j,g,:] = sum over h in group g and rows i of P_ij dO[b,i,h,:]
+ *   dq~[b,i,h,:] = scale sum_j dS_ij k~[b,j,g,:]
+ *   dk~[b,j,g,:] = scale sum over h in group g and rows i of dS_ij q~[b,i,h,:]
+ *   dq = R^T dq~, dk = R^T dk~  (R: the forward's rotation at the same
+ *   positions; identity without RoPE)
+ * P and dS enter the MFMA contractions as bf16; accumulation is fp32 and the
+ * inverse rotation fp64.  Deterministic: no atomics, the same inputs give the
+ * same bits.
+ *
+ * Arguments:
+ *   q, k, v, causal, scale, rope_base, dtype: as given to attn_fwd
+ *   o    [B, Sq, Hq, D] dtype: attn_fwd's output for these inputs
+ *   dout [B, Sq, Hq, D] dtype: gradient of the loss with respect to o
+ *   lse  [B, Hq, Sq] fp32: attn_fwd's lse for these inputs (required)
+ *   dq   [B, Sq, Hq, D] dtype, dk and dv [B, Skv, Hkv, D] dtype (outputs)
+ *   workspace: attn_bwd_workspace_bytes(...) bytes of device memory, or NULL
+ *          to use a library-owned buffer
+ *   Built: dtype ATTN_BF16 with D == 64; RoPE needs Sq <= Skv.
+ * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED (other dtype or D),
+ *   ATTN_ERR_EMPTY_KV (Skv == 0), ATTN_ERR_HIP.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+             int Skv, int D, int causal, float scale, float rope_base, int dtype,
+             void* workspace, hipStream_t stream);
 
 /*
  * attn_decode_workspace_bytes — size of the workspace attn_decode_splitkv needs

@@ -105,3 +105,40 @@ def test_workspace_bytes(lib):
     assert xa.attn_decode_workspace_bytes(1, 1, 64, 1) % 256 == 0
     assert xa.attn_decode_workspace_bytes(1, 1, 64, 1) >= 65 * 4
     assert xa.attn_decode_workspace_bytes(0, 1, 64, 1) == 0
+
+
+def _bwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1,
+         Hq=4, Hkv=2, Sq=8, Skv=8, D=64, causal=0, scale=0.125, rope=0.0, dtype=1):
+    return lib.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, causal, scale,
+                        rope, dtype, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), xa.ATTN_ERR_INVALID),
+    (dict(do=None), xa.ATTN_ERR_INVALID),
+    (dict(lse=None), xa.ATTN_ERR_INVALID),
+    (dict(dk=None), xa.ATTN_ERR_INVALID),
+    (dict(B=0), xa.ATTN_ERR_INVALID),
+    (dict(Skv=0), xa.ATTN_ERR_EMPTY_KV),
+    (dict(Hq=6, Hkv=4), xa.ATTN_ERR_INVALID),
+    (dict(causal=3), xa.ATTN_ERR_INVALID),
+    (dict(scale=0.0), xa.ATTN_ERR_INVALID),
+    (dict(rope=float("inf")), xa.ATTN_ERR_INVALID),
+    (dict(D=63, rope=100.0), xa.ATTN_ERR_INVALID),
+    (dict(dtype=9), xa.ATTN_ERR_INVALID),
+    (dict(dtype=0), xa.ATTN_ERR_UNSUPPORTED),
+    (dict(D=128), xa.ATTN_ERR_UNSUPPORTED),
+    (dict(Sq=16, Skv=8, rope=10000.0), xa.ATTN_ERR_UNSUPPORTED),
+])
+def test_bwd_validation(lib, kw, code):
+    assert _bwd(lib, **kw) == code
+    assert xa.last_error() != ""
+
+
+def test_bwd_workspace_bytes(lib):
+    stats = 2 * ((4 * 32 * 4096 * 4 + 255) // 256 * 256)
+    assert xa.attn_bwd_workspace_bytes(4, 32, 8, 4096, 4096, 64) == stats
+    rot = (4 * 4096 * 32 * 64 * 2) + (4 * 4096 * 8 * 64 * 2)
+    assert xa.attn_bwd_workspace_bytes(4, 32, 8, 4096, 4096, 64, 10000.0) == stats + rot
+    assert xa.attn_bwd_workspace_bytes(1, 1, 1, 3, 5, 64) % 256 == 0
+    assert xa.attn_bwd_workspace_bytes(0, 1, 1, 3, 5, 64) == 0

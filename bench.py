@@ -286,6 +286,26 @@ def main():
     kern_tflops = pc.flops / (kern_ms * 1e-3) / 1e12
     traffic = read_traffic(pc.io_bytes)
 
+    # ---- backward of the same prefill (next to the hot path, not in `value`):
+    # attn_bwd with the forward's O and LSE and a resident upstream gradient.
+    # Algorithmic flops = 2.5 x the forward's (the recomputed S, dP, dV, dK, dQ
+    # products against the forward's S and O); the kernels recompute S and dP
+    # once more for dQ, which is not counted.
+    dout = W.to_device(W.f32_to_bf16_bits(
+        np.random.default_rng(pc.seed + 7).standard_normal(q_np.shape, dtype=np.float32)))
+    xa.attn_fwd(q, k, v, causal=True, scale=pc.scale, rope_base=pc.rope_base, o=o, lse=lse)
+    bwd_ws = torch.empty(xa.attn_bwd_workspace_bytes(pc.B, pc.Hq, pc.Hkv, pc.Sq, pc.Skv, pc.D,
+                                                     pc.rope_base), dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def backward():
+        xa.attn_bwd(q, k, v, o, dout, lse, causal=True, scale=pc.scale, rope_base=pc.rope_base,
+                    dq=dq, dk=dk, dv=dv, workspace=bwd_ws)
+    for _ in range(3):
+        backward()
+    bwd_ms = timed(backward, max(args.steps // 2, 10), stream)
+    bwd_tflops = 2.5 * pc.flops / (bwd_ms * 1e-3) / 1e12
+
     result = {
         "metric": METRIC,
         "value": round(pre_tflops, 2),
@@ -318,6 +338,10 @@ def main():
                      "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
                      "launch_ms": round(kern_ms, 4), "traffic": traffic},
+        "backward": {"workload": "LFM2 GQA prefill backward (dq, dk, dv), RoPE, causal",
+                     "ms": round(bwd_ms, 4), "tflops": round(bwd_tflops, 2),
+                     "frac_of_mfma_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "flops": "2.5 x forward (5 products)"},
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1),
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                             "frac": round(dec_gbps / PEAK_HBM_GBPS, 4)},

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_EMPTY_KV = 0, -1, -2, -3, -4
 EXPORTS = ("attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_decode_workspace_bytes",
-           "attn_decode_splitkv", "rope_apply", "attn_last_error")
+           "attn_decode_splitkv", "attn_prefill_kvcache", "rope_apply", "attn_last_error")
 
 _lib = None
 
@@ -55,6 +55,9 @@ def load():
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp]
     lib.attn_decode_splitkv.restype = i
+    lib.attn_prefill_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
+                                         f, vp]
+    lib.attn_prefill_kvcache.restype = i
     lib.rope_apply.argtypes = [vp, i, i, i, i, i, f, i, vp]
     lib.rope_apply.restype = i
     lib.attn_last_error.argtypes = []
@@ -187,6 +190,36 @@ def attn_decode_splitkv(q, kcache, vcache, seqlens, num_splits, scale=None, o=No
     _check(load().attn_decode_splitkv(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(o),
                                       B, Hq, Hkv, D, int(num_splits), float(scale), Smax,
                                       _ptr(lse), _ptr(workspace), _stream(stream)))
+    return o, lse
+
+
+def attn_prefill_kvcache(q, k_new, v_new, kcache, vcache, cache_lens, causal=True, scale=None,
+                         rope_base=0.0, o=None, lse=None, stream=None, want_lse=True):
+    """Append (k_new, v_new) to the caches after cache_lens[b] rows (keys
+    rotated at their positions), then attend q to the first cache_lens[b] + Sq
+    rows.  q [B,Sq,Hq,D], k_new/v_new [B,Sq,Hkv,D], caches [B,Smax,Hkv,D]
+    (bf16), cache_lens [B] int32 (not updated).  Returns (o, lse)."""
+    _need_gpu(q, k_new, v_new, kcache, vcache, cache_lens, o, lse)
+    B, Sq, Hq, D = q.shape
+    Bc, Smax, Hkv, Dc = kcache.shape
+    if tuple(vcache.shape) != tuple(kcache.shape) or Bc != B or Dc != D:
+        raise ValueError("cache shape mismatch")
+    if tuple(k_new.shape) != (B, Sq, Hkv, D) or tuple(v_new.shape) != (B, Sq, Hkv, D):
+        raise ValueError("k_new / v_new must be [B, Sq, Hkv, D]")
+    if cache_lens.dtype != torch.int32 or tuple(cache_lens.shape) != (B,):
+        raise ValueError("cache_lens must be int32 [B]")
+    if not (q.dtype == k_new.dtype == v_new.dtype == kcache.dtype == vcache.dtype == torch.bfloat16):
+        raise TypeError("bf16 tensors expected")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(load().attn_prefill_kvcache(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kcache),
+                                       _ptr(vcache), _ptr(cache_lens), _ptr(o), _ptr(lse), B, Hq,
+                                       Hkv, Sq, D, Smax, int(bool(causal)), float(scale),
+                                       float(rope_base), _stream(stream)))
     return o, lse
 
 

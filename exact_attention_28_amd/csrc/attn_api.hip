@@ -261,6 +261,59 @@ int attn_decode_splitkv(const void* q, const void* kcache, const void* vcache,
   return hip_status(e, "attn_decode_splitkv: kernel launch");
 }
 
+int attn_prefill_kvcache(const void* q, const void* k_new, const void* v_new, void* kcache,
+                         void* vcache, const int* cache_lens, void* o, float* lse, int B, int Hq,
+                         int Hkv, int Sq, int D, int max_seqlen, int causal, float scale,
+                         float rope_base, hipStream_t stream) {
+  if (!q || !k_new || !v_new || !kcache || !vcache || !cache_lens || !o)
+    return fail(ATTN_ERR_INVALID,
+                "attn_prefill_kvcache: null q, k_new, v_new, kcache, vcache, cache_lens or o");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || D < 1 || max_seqlen < 1)
+    return fail(ATTN_ERR_INVALID, "attn_prefill_kvcache: sizes must be >= 1");
+  if (Sq > max_seqlen)
+    return fail(ATTN_ERR_INVALID, "attn_prefill_kvcache: Sq=%d exceeds max_seqlen=%d", Sq,
+                max_seqlen);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_INVALID, "attn_prefill_kvcache: Hq=%d is not a multiple of Hkv=%d", Hq,
+                Hkv);
+  if (causal != 0 && causal != 1)
+    return fail(ATTN_ERR_INVALID, "attn_prefill_kvcache: causal must be 0 or 1");
+  if (!finite_pos(scale))
+    return fail(ATTN_ERR_INVALID, "attn_prefill_kvcache: scale must be finite and > 0");
+  if (std::isnan(rope_base) || std::isinf(rope_base))
+    return fail(ATTN_ERR_INVALID, "attn_prefill_kvcache: rope_base must be finite");
+  const bool rope = rope_base > 0.f;
+  if (rope && D % 2 != 0)
+    return fail(ATTN_ERR_INVALID, "attn_prefill_kvcache: RoPE needs an even head dim");
+  if (D != 64 && D != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_kvcache: D=%d (built: 64, 128)", D);
+  if ((long long)max_seqlen * Hkv * D * 2 >= 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_kvcache: one batch's cache exceeds 2 GiB");
+  if ((long long)B * Hq * ((Sq + 15) / 16) > 0x7fffffffLL || B > 65535 || Hq > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_kvcache: grid too large");
+
+  const double2* tab = nullptr;
+  if (rope) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    int st;
+    DevBuffers* db = buffers(&st);
+    if (!db) return st;
+    const size_t tab_bytes = (size_t)max_seqlen * (D / 2) * sizeof(double2);
+    if ((st = grow(&db->rope_tab, &db->rope_tab_bytes, tab_bytes, "rope table")) != ATTN_OK)
+      return st;
+    tab = static_cast<const double2*>(db->rope_tab);
+    hipError_t e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), 0, max_seqlen, D,
+                                            (double)rope_base, stream);
+    if (e != hipSuccess) return hip_status(e, "attn_prefill_kvcache: rope table launch");
+  }
+  hipError_t e = xattn::launch_cache_append(k_new, v_new, kcache, vcache, cache_lens, B, Sq, Hkv,
+                                            D, max_seqlen, tab, stream);
+  if (e != hipSuccess) return hip_status(e, "attn_prefill_kvcache: append launch");
+  e = xattn::launch_fwd_bf16(q, kcache, vcache, o, lse, B, Hq, Hkv, Sq, max_seqlen, D, causal,
+                             scale, tab, stream, cache_lens, max_seqlen);
+  return hip_status(e, "attn_prefill_kvcache: kernel launch");
+}
+
 int rope_apply(void* x, int B, int S, int H, int D, int pos_offset, float rope_base, int dtype,
                hipStream_t stream) {
   if (!x) return fail(ATTN_ERR_INVALID, "rope_apply: null x");

@@ -77,8 +77,9 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buf
 template <int D, int HPW, bool CAUSAL, bool ROPE, int NQB>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
-    u16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Skv,
-    float scale_log2, const double2* __restrict__ tab, int n_qt, int n_bh) {
+    u16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Skv_all,
+    const int* __restrict__ kv_lens, int kv_rows, float scale_log2,
+    const double2* __restrict__ tab, int n_qt, int n_bh) {
   constexpr int BM = 128 * NQB, BN = 64, NP = BM / HPW;
   constexpr int KCH = D / 8;                 // 16-byte chunks per row
   constexpr int LD = BN * KCH / 256;         // 16-byte chunks per thread per tile (K and V each)
@@ -109,6 +110,10 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   const int h0 = (bh % HG) * HPW;
   const int kvh = h0 / (Hq / Hkv);
   const int p0 = qt * NP;
+  // Keys of this batch: Skv_all, or with a cache (kv_lens non-null) the
+  // batch's cached rows (clamped to the capacity) plus the Sq new ones.  K and
+  // V hold kv_rows rows per batch.
+  const int Skv = kv_lens ? min(max(kv_lens[b], 0), kv_rows - Sq) + Sq : Skv_all;
   const int off = Skv - Sq;
 
   // this lane's query columns: qb-th block of 32 columns of wave w
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
 
   // K and V of this (batch, kv head) through range-checked buffer resources:
   // rows at or past Skv read as zero, offsets are 32-bit.
-  const long long head_base = (long long)b * Skv * Hkv * D + (long long)kvh * D;
+  const long long head_base = (long long)b * kv_rows * Hkv * D + (long long)kvh * D;
   const uint32_t nbytes = (uint32_t)(((long long)Skv * Hkv * D - (long long)kvh * D) * 2);
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc((void*)(K + head_base), (short)0, nbytes, kBufferWord3);
@@ -355,8 +360,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
 
 template <int D, int HPW, bool CAUSAL, bool ROPE, int NQB>
 static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                          int Hq, int Hkv, int Sq, int Skv, float scale, const double2* tab,
-                          hipStream_t stream) {
+                          int Hq, int Hkv, int Sq, int Skv, const int* kv_lens, int kv_rows,
+                          float scale, const double2* tab, hipStream_t stream) {
   constexpr int NP = 128 * NQB / HPW;
   const int n_qt = (Sq + NP - 1) / NP;
   const int n_bh = B * (Hq / HPW);
@@ -364,7 +369,8 @@ static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, 
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   fwd_bf16_kernel<D, HPW, CAUSAL, ROPE, NQB><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
       static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v),
-      static_cast<u16*>(o), lse, Hq, Hkv, Sq, Skv, scale * kLog2e, tab, n_qt, n_bh);
+      static_cast<u16*>(o), lse, Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale * kLog2e, tab, n_qt,
+      n_bh);
   return hipGetLastError();
 }
 
@@ -373,37 +379,44 @@ static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, 
 // workgroups (at least two per CU).
 template <int D, int HPW, bool CAUSAL, bool ROPE>
 static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                          int Hq, int Hkv, int Sq, int Skv, float scale, const double2* tab,
-                          hipStream_t stream) {
+                          int Hq, int Hkv, int Sq, int Skv, const int* kv_lens, int kv_rows,
+                          float scale, const double2* tab, hipStream_t stream) {
   const long long wg2 = (long long)((Sq + 256 / HPW - 1) / (256 / HPW)) * B * (Hq / HPW);
   if (D == 64 && wg2 >= 2 * 256)
-    return go_bf16<D, HPW, CAUSAL, ROPE, 2>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab,
-                                            stream);
-  return go_bf16<D, HPW, CAUSAL, ROPE, 1>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab,
-                                          stream);
+    return go_bf16<D, HPW, CAUSAL, ROPE, 2>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
+                                            kv_rows, scale, tab, stream);
+  return go_bf16<D, HPW, CAUSAL, ROPE, 1>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
+                                          scale, tab, stream);
 }
 
 template <int D, bool CAUSAL, bool ROPE>
 static hipError_t pick_hpw(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int Hq, int Hkv, int Sq, int Skv, float scale,
-                           const double2* tab, hipStream_t stream) {
+                           int B, int Hq, int Hkv, int Sq, int Skv, const int* kv_lens,
+                           int kv_rows, float scale, const double2* tab, hipStream_t stream) {
   const int G = Hq / Hkv;
   if (G % 8 == 0)
-    return go_bf16<D, 8, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab, stream);
+    return go_bf16<D, 8, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
+                                       scale, tab, stream);
   if (G % 4 == 0)
-    return go_bf16<D, 4, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab, stream);
+    return go_bf16<D, 4, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
+                                       scale, tab, stream);
   if (G % 2 == 0)
-    return go_bf16<D, 2, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab, stream);
-  return go_bf16<D, 1, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab, stream);
+    return go_bf16<D, 2, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
+                                       scale, tab, stream);
+  return go_bf16<D, 1, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
+                                     scale, tab, stream);
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
-                           float scale, const double2* rope_tab, hipStream_t stream) {
+                           float scale, const double2* rope_tab, hipStream_t stream,
+                           const int* kv_lens, int kv_rows) {
   const bool rope = rope_tab != nullptr;
+  if (kv_lens == nullptr) kv_rows = Skv;
 #define XATTN_BF16_CASE(DD, C, R)                                                          \
   if (D == DD && (causal != 0) == C && rope == R)                                        \
-    return pick_hpw<DD, C, R>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, rope_tab, stream);
+    return pick_hpw<DD, C, R>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale, \
+                              rope_tab, stream);
   XATTN_BF16_CASE(64, false, false)
   XATTN_BF16_CASE(64, true, false)
   XATTN_BF16_CASE(64, false, true)

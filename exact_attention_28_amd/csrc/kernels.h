@@ -10,9 +10,21 @@ namespace xattn {
 // rope_tab: table rows for positions [0, Skv); query row i uses row Skv-Sq+i.
 // bf16 rotates only the queries in the kernel (keys arrive rotated); fp32
 // rotates queries and keys.  Null disables rotation.
+// bf16 with kv_lens non-null: k/v are caches of kv_rows rows per batch and
+// batch b attends to its first min(kv_lens[b], kv_rows - Sq) + Sq rows (Skv
+// is then unused; the table must cover kv_rows positions).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
-                           float scale, const double2* rope_tab, hipStream_t stream);
+                           float scale, const double2* rope_tab, hipStream_t stream,
+                           const int* kv_lens = nullptr, int kv_rows = 0);
+
+// Cache append: rows t < Sq of k_new/v_new [B,Sq,Hkv,D] (bf16) go to rows
+// L_b + t of kcache/vcache [B,rows,Hkv,D] with L_b = min(max(lens[b], 0),
+// rows - Sq); keys are rotated at position L_b + t (table row L_b + t, fp64,
+// rounded to bf16) when tab is non-null.
+hipError_t launch_cache_append(const void* k_new, const void* v_new, void* kcache, void* vcache,
+                               const int* lens, int B, int Sq, int Hkv, int D, int rows,
+                               const double2* tab, hipStream_t stream);
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                           int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
                           float scale, const double2* rope_tab, hipStream_t stream);

@@ -176,6 +176,42 @@ int attn_decode_splitkv(const void* q, const void* kcache, const void* vcache,
                         void* workspace, hipStream_t stream);
 
 /*
+ * attn_prefill_kvcache — one chunk of a streaming (chunked) prefill against a
+ * token-major KV cache: append, then attend.
+ *
+ * For batch b, with L_b = cache_lens[b] positions already in the cache (keys
+ * stored rotated, as this call stores them):
+ *  1. kcache[b, L_b + t, g, :] = R(L_b + t) k_new[b, t, g, :] (fp64 rotation
+ *     rounded to bf16) and vcache[b, L_b + t, g, :] = v_new[b, t, g, :] for
+ *     t < Sq — the position_offset of [GQA] RotaryPositionEmbedding::apply and
+ *     the cache append of [GQA] forward_with_cache;
+ *  2. O and lse of q[b, i] (rotated at position L_b + i) against cache rows
+ *     [0, L_b + Sq): exactly attn_fwd with Skv = L_b + Sq (bottom-right causal:
+ *     key j is hidden from row i iff j > L_b + i, the cached-generation rule
+ *     of [GQA] forward_with_cache).
+ * Sq == 1 is one decode step that also appends its token.  The call does not
+ * update cache_lens: the caller adds Sq once the call is ordered before the
+ * next use.  Without RoPE (rope_base <= 0) nothing is rotated.
+ *
+ * Arguments:
+ *   q [B, Sq, Hq, D] bf16;  k_new, v_new [B, Sq, Hkv, D] bf16
+ *   kcache, vcache [B, max_seqlen, Hkv, D] bf16 (rows < L_b are read, rows
+ *          [L_b, L_b + Sq) written, later rows neither read nor written)
+ *   cache_lens [B] int32 in device memory, 0 <= cache_lens[b] <= max_seqlen - Sq
+ *          (a precondition, as for attn_decode_splitkv: values outside are
+ *          clamped into that range)
+ *   o [B, Sq, Hq, D] bf16 (output);  lse [B, Hq, Sq] fp32 (output, may be NULL)
+ *   B, Hq, Hkv, Sq >= 1; Hq % Hkv == 0; D in {64, 128}; 1 <= Sq <= max_seqlen;
+ *   causal 0 or 1; scale finite and > 0; rope_base > 0 enables RoPE (D even)
+ * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP.  With RoPE the
+ *   call rebuilds the library's RoPE table for max_seqlen positions.
+ */
+int attn_prefill_kvcache(const void* q, const void* k_new, const void* v_new, void* kcache,
+                         void* vcache, const int* cache_lens, void* o, float* lse, int B, int Hq,
+                         int Hkv, int Sq, int D, int max_seqlen, int causal, float scale,
+                         float rope_base, hipStream_t stream);
+
+/*
  * rope_apply — rotary position embedding, in place ([GQA]
  * RotaryPositionEmbedding::apply with its position_offset argument).
  *

@@ -142,3 +142,27 @@ def test_bwd_workspace_bytes(lib):
     assert xa.attn_bwd_workspace_bytes(4, 32, 8, 4096, 4096, 64, 10000.0) == stats + rot
     assert xa.attn_bwd_workspace_bytes(1, 1, 1, 3, 5, 64) % 256 == 0
     assert xa.attn_bwd_workspace_bytes(0, 1, 1, 3, 5, 64) == 0
+
+
+def _pkv(lib, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, o=FAKE, B=2, Hq=8, Hkv=2,
+         Sq=16, D=64, smax=128, causal=1, scale=0.125, rope=10000.0):
+    return lib.attn_prefill_kvcache(q, kn, vn, kc, vc, lens, o, None, B, Hq, Hkv, Sq, D, smax,
+                                    causal, scale, rope, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kc=None), xa.ATTN_ERR_INVALID),
+    (dict(lens=None), xa.ATTN_ERR_INVALID),
+    (dict(o=None), xa.ATTN_ERR_INVALID),
+    (dict(B=0), xa.ATTN_ERR_INVALID),
+    (dict(Sq=0), xa.ATTN_ERR_INVALID),
+    (dict(Sq=200, smax=128), xa.ATTN_ERR_INVALID),
+    (dict(Hq=8, Hkv=3), xa.ATTN_ERR_INVALID),
+    (dict(causal=5), xa.ATTN_ERR_INVALID),
+    (dict(scale=float("nan")), xa.ATTN_ERR_INVALID),
+    (dict(D=63, rope=10000.0), xa.ATTN_ERR_INVALID),
+    (dict(D=96, rope=0.0), xa.ATTN_ERR_UNSUPPORTED),
+])
+def test_prefill_kvcache_validation(lib, kw, code):
+    assert _pkv(lib, **kw) == code
+    assert xa.last_error() != ""

@@ -306,6 +306,29 @@ def main():
     bwd_ms = timed(backward, max(args.steps // 2, 10), stream)
     bwd_tflops = 2.5 * pc.flops / (bwd_ms * 1e-3) / 1e12
 
+    # ---- the same prefill as four 1024-token chunks through a KV cache
+    # (attn_prefill_kvcache: append + attention per chunk); same flops as the
+    # one-shot prefill.
+    CH = 1024
+    kc_, vc_ = torch.empty_like(k), torch.empty_like(v)
+    lens = torch.zeros(pc.B, dtype=torch.int32, device="cuda")
+    qch = [q[:, c0:c0 + CH].contiguous() for c0 in range(0, pc.Sq, CH)]
+    kch = [k[:, c0:c0 + CH].contiguous() for c0 in range(0, pc.Sq, CH)]
+    vch = [v[:, c0:c0 + CH].contiguous() for c0 in range(0, pc.Sq, CH)]
+    och = [torch.empty_like(x) for x in qch]
+
+    def chunked():
+        lens.zero_()
+        for i in range(len(qch)):
+            xa.attn_prefill_kvcache(qch[i], kch[i], vch[i], kc_, vc_, lens, causal=True,
+                                    scale=pc.scale, rope_base=pc.rope_base, o=och[i],
+                                    want_lse=False)
+            lens.add_(CH)
+    for _ in range(3):
+        chunked()
+    ch_ms = timed(chunked, max(args.steps // 2, 10), stream)
+    ch_tflops = pc.flops / (ch_ms * 1e-3) / 1e12
+
     result = {
         "metric": METRIC,
         "value": round(pre_tflops, 2),
@@ -342,6 +365,10 @@ def main():
                      "ms": round(bwd_ms, 4), "tflops": round(bwd_tflops, 2),
                      "frac_of_mfma_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "flops": "2.5 x forward (5 products)"},
+        "chunked_prefill": {"workload": "LFM2 GQA prefill as 4 chunks of 1024 tokens through "
+                                        "a KV cache (append + attention per chunk)",
+                            "ms": round(ch_ms, 4), "tflops": round(ch_tflops, 2),
+                            "frac_of_mfma_peak": round(ch_tflops / PEAK_BF16_TFLOPS, 4)},
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1),
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                             "frac": round(dec_gbps / PEAK_HBM_GBPS, 4)},

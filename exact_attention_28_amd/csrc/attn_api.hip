@@ -49,6 +49,8 @@ struct DevBuffers {
   size_t dec_ws_bytes = 0;
   void* bwd_ws = nullptr;
   size_t bwd_ws_bytes = 0;
+  void* pad_ws = nullptr;
+  size_t pad_ws_bytes = 0;
 };
 
 std::mutex g_mu;
@@ -90,6 +92,54 @@ int hip_status(hipError_t e, const char* what) {
   return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// attn_fwd for a head dim other than 64 and 128: zero-padded copies of Q, K,
+// V (Q and K rotated with the angles of the true D), the kernel at the padded
+// width without rotation, then O's first D columns.
+int fwd_padded(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+               int Hkv, int Sq, int Skv, int D, int causal, float scale, float rope_base,
+               int dtype, hipStream_t stream) {
+  const int Dp = D <= 64 ? 64 : 128;
+  const size_t es = dtype == ATTN_BF16 ? 2 : 4;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t qb = up((size_t)B * Sq * Hq * Dp * es), kb = up((size_t)B * Skv * Hkv * Dp * es);
+  std::lock_guard<std::mutex> lock(g_mu);
+  int st;
+  DevBuffers* db = buffers(&st);
+  if (!db) return st;
+  if ((st = grow(&db->pad_ws, &db->pad_ws_bytes, 2 * qb + 2 * kb, "padded head dim staging")) !=
+      ATTN_OK)
+    return st;
+  char* base = static_cast<char*>(db->pad_ws);
+  void *qp = base, *kp = base + qb, *vp = base + qb + kb, *op = base + qb + 2 * kb;
+  const double2* tab = nullptr;
+  hipError_t e;
+  if (rope_base > 0.f) {
+    const size_t tab_bytes = (size_t)Skv * (D / 2) * sizeof(double2);
+    if ((st = grow(&db->rope_tab, &db->rope_tab_bytes, tab_bytes, "rope table")) != ATTN_OK)
+      return st;
+    tab = static_cast<const double2*>(db->rope_tab);
+    e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), 0, Skv, D,
+                                 (double)rope_base, stream);
+    if (e != hipSuccess) return hip_status(e, "attn_fwd: rope table launch");
+  }
+  const int dt = dtype == ATTN_BF16 ? 1 : 0;
+  if ((e = xattn::launch_pack_heads(q, qp, B, Sq, Hq, D, Dp, tab, Skv - Sq, dt, stream)) !=
+          hipSuccess ||
+      (e = xattn::launch_pack_heads(k, kp, B, Skv, Hkv, D, Dp, tab, 0, dt, stream)) != hipSuccess ||
+      (e = xattn::launch_pack_heads(v, vp, B, Skv, Hkv, D, Dp, nullptr, 0, dt, stream)) !=
+          hipSuccess)
+    return hip_status(e, "attn_fwd: head-dim padding launch");
+  if (dtype == ATTN_BF16)
+    e = xattn::launch_fwd_bf16(qp, kp, vp, op, lse, B, Hq, Hkv, Sq, Skv, Dp, causal, scale,
+                               nullptr, stream);
+  else
+    e = xattn::launch_fwd_f32(qp, kp, vp, op, lse, B, Hq, Hkv, Sq, Skv, Dp, causal, scale,
+                              nullptr, stream);
+  if (e != hipSuccess) return hip_status(e, "attn_fwd: kernel launch");
+  e = xattn::launch_unpack_heads(op, o, (long long)B * Sq * Hq, D, Dp, dt, stream);
+  return hip_status(e, "attn_fwd: head-dim unpadding launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,12 +164,15 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (rope && D % 2 != 0) return fail(ATTN_ERR_INVALID, "attn_fwd: RoPE needs an even head dim");
   if (dtype != ATTN_F32 && dtype != ATTN_BF16)
     return fail(ATTN_ERR_INVALID, "attn_fwd: unknown dtype %d", dtype);
-  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: D=%d (built: 64, 128)", D);
+  if (D > 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: D=%d (built: up to 128)", D);
   if (rope && Sq > Skv)
     return fail(ATTN_ERR_UNSUPPORTED,
                 "attn_fwd: RoPE with Sq > Skv would place queries at negative positions");
   if ((long long)B * Hq * ((Sq + 15) / 16) > 0x7fffffffLL || B > 65535 || Hq > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: grid too large");
+  if (D != 64 && D != 128)
+    return fwd_padded(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, rope_base, dtype,
+                      stream);
 
   const double2* tab = nullptr;
   const void* kin = k;

@@ -49,6 +49,15 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            float scale, const double2* rope_tab, void* workspace,
                            hipStream_t stream);
 
+// Head dims other than 64/128: copy x [B,S,H,D] into y [B,S,H,Dp] with zero
+// columns past D (dtype 0 fp32 / 1 bf16), rotating pair i < D/2 of token t by
+// table row pos0 + t when tab is non-null; and back: o [rows, D] from the first
+// D columns of op [rows, Dp].
+hipError_t launch_pack_heads(const void* x, void* y, int B, int S, int H, int D, int Dp,
+                             const double2* tab, int pos0, int dtype, hipStream_t stream);
+hipError_t launch_unpack_heads(const void* op, void* o, long long rows, int D, int Dp, int dtype,
+                               hipStream_t stream);
+
 // Decode: split pass into the workspace, then the merge pass.
 size_t decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int* seqlens,

@@ -79,7 +79,12 @@ typedef enum {
  * Arguments:
  *   q    [B, Sq, Hq, D]  dtype          k, v [B, Skv, Hkv, D] dtype
  *   o    [B, Sq, Hq, D]  dtype (output) lse  [B, Hq, Sq] fp32 (output; may be NULL)
- *   B, Hq, Hkv, Sq, Skv, D >= 1; Hq % Hkv == 0; D in {64, 128}
+ *   B, Hq, Hkv, Sq, Skv, D >= 1; Hq % Hkv == 0; D <= 128.  D = 64 and 128 run
+ *   the kernels directly; any other D runs them on zero-padded copies (64 or
+ *   128 columns; Q and K rotated with the angles of the true D), which is
+ *   exact: the head-dim padding of [LF] GqaConfig::pad_head_dim_to (36 -> 40
+ *   for Moonshine), with the scale passed explicitly (1/sqrt(D), not the
+ *   padded width's).  The padded copies live in a library-owned buffer.
  *   causal: 0 or 1;  scale: finite and > 0, used as given (the pages' default
  *   is 1/sqrt(D));  rope_base: > 0 enables RoPE (D even), <= 0 disables it
  *   dtype: ATTN_BF16 (bf16 MFMA, fp32 accumulation) or ATTN_F32 (fp32 throughout)

@@ -434,6 +434,26 @@ def pin_sampled_rows(lib):
         np.testing.assert_array_equal(ls[ui], lse[b, h, rows])
 
 
+def pin_padded_head_dim(lib):
+    """Zero-padding the head dim (36 -> 40) and multiplying Q by sqrt(40/36)
+    under the scale 1/sqrt(40) gives exact attention at D = 36 with the scale
+    1/sqrt(36): zero columns add nothing to the scores, V's zero columns give
+    zero output columns, and the two scales agree."""
+    rng = np.random.default_rng(33)
+    for (B, Hq, Hkv, Sq, Skv, causal) in ((1, 8, 2, 3, 7, False), (2, 4, 1, 6, 6, True)):
+        D, Dp = 36, 40
+        q, k, v = _rand(rng, B, Sq, Hq, D), _rand(rng, B, Skv, Hkv, D), _rand(rng, B, Skv, Hkv, D)
+        o, lse = oracle.attn_fwd(q, k, v, causal=causal, scale=1 / math.sqrt(D), lib=lib)
+
+        def pad(x):
+            return np.concatenate([x, np.zeros(x.shape[:-1] + (Dp - D,))], axis=-1)
+        op, lsep = oracle.attn_fwd(pad(q * math.sqrt(Dp / D)), pad(k), pad(v), causal=causal,
+                                   scale=1 / math.sqrt(Dp), lib=lib)
+        np.testing.assert_allclose(op[..., :D], o, atol=1e-12)
+        assert (op[..., D:] == 0).all()
+        np.testing.assert_allclose(lsep, lse, atol=1e-12)
+
+
 # ---------------------------------------------------------- backward --
 
 def _torch_rope(x, pos0, base):

@@ -56,8 +56,8 @@ def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=4, Hkv=2, Sq=8, 
     (dict(rope=float("nan")), xa.ATTN_ERR_INVALID),
     (dict(D=63, rope=10000.0), xa.ATTN_ERR_INVALID),
     (dict(dtype=7), xa.ATTN_ERR_INVALID),
-    (dict(D=96), xa.ATTN_ERR_UNSUPPORTED),
-    (dict(D=32), xa.ATTN_ERR_UNSUPPORTED),
+    (dict(D=129), xa.ATTN_ERR_UNSUPPORTED),
+    (dict(D=256), xa.ATTN_ERR_UNSUPPORTED),
     (dict(Sq=16, Skv=8, rope=10000.0), xa.ATTN_ERR_UNSUPPORTED),
 ])
 def test_attn_fwd_validation(lib, kw, code):

@@ -326,3 +326,38 @@ def test_decode_equals_last_prefill_row():
     torch.cuda.synchronize()
     np.testing.assert_allclose(_np(od), o[:, -1], atol=2e-2)
     np.testing.assert_allclose(_np(lsed), lse[:, :, -1], atol=1e-3)
+
+
+# ------------------------------------------------- other head dims (padded) --
+
+PAD_CASES = [  # dtype, B, Hq, Hkv, Sq, Skv, D, causal, rope
+    ("bf16", 2, 8, 2, 3, 7, 36, False, 0.0),        # Moonshine-tiny cross-attention shape
+    ("bf16", 2, 8, 2, 64, 1500, 36, False, 0.0),    # decoder queries against 1500 encoder frames
+    ("bf16", 1, 8, 2, 130, 130, 36, True, 10000.0),  # decoder self-attention, RoPE at D = 36
+    ("bf16", 1, 4, 4, 77, 200, 80, True, 10000.0),
+    ("bf16", 2, 2, 1, 50, 50, 1, False, 0.0),
+    ("bf16", 1, 3, 3, 65, 65, 127, True, 0.0),
+    ("f32", 1, 8, 2, 40, 90, 36, False, 0.0),
+    ("f32", 1, 4, 2, 70, 70, 100, True, 500.0),
+]
+
+
+@pytest.mark.parametrize("case", PAD_CASES, ids=[str(c) for c in PAD_CASES])
+def test_padded_head_dims(case):
+    """Head dims other than 64 and 128 run the kernels on zero-padded copies;
+    the result must meet the same bars as the native dims."""
+    dt, B, Hq, Hkv, Sq, Skv, D, causal, rope = case
+    say("case padded", case)
+    rng = np.random.default_rng(abs(hash(case)) % 2 ** 32)
+    f = [rng.standard_normal(s, dtype=np.float32)
+         for s in ((B, Sq, Hq, D), (B, Skv, Hkv, D), (B, Skv, Hkv, D))]
+    q, k, v = f if dt == "f32" else [W.f32_to_bf16_bits(x) for x in f]
+    scale = float(np.float32(1 / math.sqrt(D)))
+    o, lse = run_fwd(q, k, v, causal, scale, rope)
+    assert o.shape == (B, Sq, Hq, D)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal=causal, scale=scale, rope_base=rope,
+                                     nthreads=NTHREADS)
+    if dt == "f32":
+        check_f32(o, lse, o_ref, lse_ref, str(case))
+    else:
+        check_bf16(o, lse, o_ref, lse_ref, str(case))

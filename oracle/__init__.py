@@ -41,8 +41,9 @@ def load(path=None):
 
 def _declare(lib):
     vp, i, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+    ll = ctypes.c_longlong
     lib.oracle_attn_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, d, d, i, _ip, i, _ip, i,
-                                    _dp, _dp, i]
+                                    _dp, _dp, _dp, ll, ll, i]
     lib.oracle_attn_fwd.restype = i
     lib.oracle_decode.argtypes = [vp, vp, vp, i, _ip, i, i, i, i, i, d, _ip, i, _dp, _dp, i]
     lib.oracle_decode.restype = i
@@ -94,14 +95,16 @@ def default_round_bits(dtype_code):
 
 
 def attn_fwd(q, k, v, causal=False, scale=None, rope_base=0.0, round_bits=None, rows=None,
-             units=None, nthreads=1, lib=None):
+             units=None, nthreads=1, lib=None, mask=None):
     """Exact attention.  q [B,Sq,Hq,D], k and v [B,Skv,Hkv,D] (same dtype).
 
     Returns (o, lse).  With rows and units both None: o [B,Sq,Hq,D] and
     lse [B,Hq,Sq].  Otherwise o [len(units), len(rows), D] and
     lse [len(units), len(rows)] where a unit is b*Hq + h (None = all units /
     all rows).  round_bits: significant bits the rotated q/k are rounded to
-    (default: the input format's).
+    (default: the input format's).  mask: additive mask [Bm, Hm, Sq, Skv]
+    with Bm in (1, B) and Hm in (1, Hq) (size 1 broadcasts), added to the
+    scaled scores.
     """
     lib = lib or load()
     q, dt = _as_input(q)
@@ -122,12 +125,21 @@ def attn_fwd(q, k, v, causal=False, scale=None, rope_base=0.0, round_bits=None, 
     nu = nunits if units_a is not None else B * Hq
     o = np.empty((nu, nr, D), dtype=np.float64)
     lse = np.empty((nu, nr), dtype=np.float64)
+    mbs = mhs = 0
+    if mask is not None:
+        mask = _f64(mask)
+        Bm, Hm, Sm, Km = mask.shape
+        if Bm not in (1, B) or Hm not in (1, Hq) or Sm != Sq or Km != Skv:
+            raise ValueError(f"mask shape {mask.shape} for B={B} Hq={Hq} Sq={Sq} Skv={Skv}")
+        mhs = Sq * Skv if Hm > 1 else 0
+        mbs = Hm * Sq * Skv if Bm > 1 else 0
     st = lib.oracle_attn_fwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, dt, B, Hq, Hkv, Sq,
                              Skv, D, int(bool(causal)), float(scale), float(rope_base),
                              int(round_bits),
                              _ptr(rows_a, _ip) if rows_a is not None else None, nrows,
                              _ptr(units_a, _ip) if units_a is not None else None, nunits,
-                             _ptr(o), _ptr(lse), int(nthreads))
+                             _ptr(o), _ptr(lse), _ptr(mask) if mask is not None else None,
+                             mbs, mhs, int(nthreads))
     if st != 0:
         raise ValueError(f"oracle_attn_fwd rejected its arguments (status {st})")
     if rows is None and units is None:

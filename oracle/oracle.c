@@ -126,12 +126,16 @@ typedef struct {
   const int* units; /* b*Hq + h to evaluate (NULL: all) */
   int nunits;
   double *o, *lse; /* [nunits][nrows][D], [nunits][nrows] */
+  const double* mask; /* additive, row (b, h, i) at b*mbs + h*mhs + i*Skv (NULL: none) */
+  long long mbs, mhs;
   int nthreads, tid;
   int status;
 } fwd_job;
 
 /* One (batch, query head): the definition, written out.
- *   s_ij = scale * <q~_i, k~_j>,  s_ij = -inf where masked,
+ *   s_ij = scale * <q~_i, k~_j> + mask_ij,  s_ij = -inf where causally hidden,
+ * (the additive mask of [WH] compute_block_scores / scaled_dot_product_attention,
+ * added to the scaled score; 0 without a mask)
  *   m_i = max_j s_ij,  l_i = sum_j exp(s_ij - m_i),
  *   O_i = sum_j exp(s_ij - m_i) v_j / l_i,  LSE_i = m_i + ln l_i. */
 static int fwd_unit(const fwd_job* J, int u_slot, int unit) {
@@ -182,6 +186,13 @@ static int fwd_unit(const fwd_job* J, int u_slot, int unit) {
       double s = dot; /* planted: scale dropped */
 #else
       double s = J->scale * dot;
+#endif
+#if MUT == 11
+      if (J->mask) s += J->scale * J->mask[(size_t)b * J->mbs + (size_t)h * J->mhs + (size_t)i * Skv + j];
+#elif MUT == 12
+      if (J->mask) s += J->mask[(size_t)b * J->mbs + (size_t)h * J->mhs + (size_t)j * Sq + i];
+#else
+      if (J->mask) s += J->mask[(size_t)b * J->mbs + (size_t)h * J->mhs + (size_t)i * Skv + j];
 #endif
 #if MUT == 2
       int hidden = J->causal && j > i; /* planted: top-left alignment */
@@ -240,12 +251,15 @@ static void* fwd_worker(void* arg) {
 
 /* Attention over [B,Sq,Hq,D] queries and [B,Skv,Hkv,D] keys/values.  Outputs are
  * ordered by unit then row: o[u][r][d], lse[u][r].  `units` lists b*Hq + h and
- * `rows` lists query rows; NULL means all of them.  Units are spread over
- * `nthreads` threads; each unit is computed by exactly one thread. */
+ * `rows` lists query rows; NULL means all of them.  `mask` (NULL: none) is an
+ * fp64 additive mask whose row for (b, h, i) starts at
+ * b*mask_bstride + h*mask_hstride + i*Skv (a zero stride broadcasts).  Units are
+ * spread over `nthreads` threads; each unit is computed by exactly one thread. */
 int oracle_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
                     int Hkv, int Sq, int Skv, int D, int causal, double scale,
                     double rope_base, int round_bits, const int* rows, int nrows,
-                    const int* units, int nunits, double* o, double* lse, int nthreads) {
+                    const int* units, int nunits, double* o, double* lse, const double* mask,
+                    long long mask_bstride, long long mask_hstride, int nthreads) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1) return -1;
   if (Hq % Hkv != 0) return -1;
   if (rope_base > 0.0 && D % 2 != 0) return -1;
@@ -255,7 +269,8 @@ int oracle_attn_fwd(const void* q, const void* k, const void* v, int dtype, int 
   if (!jobs || !th) { free(jobs); free(th); return -2; }
   for (int t = 0; t < nthreads; ++t) {
     fwd_job j = {q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, causal, scale, rope_base,
-                 round_bits, rows, nrows, units, nunits, o, lse, nthreads, t, 0};
+                 round_bits, rows, nrows, units, nunits, o, lse, mask, mask_bstride,
+                 mask_hstride, nthreads, t, 0};
     jobs[t] = j;
   }
   int status = 0;

@@ -75,6 +75,12 @@ def pin_golden_whisper_mask(lib):
     assert abs(o[0, 0, 0, 0] - g["printed"]["o[0][0]"]) < g["printed"]["tolerance"]
     np.testing.assert_allclose(o[0, :, 0, :], np.array(g["derived"]["o"]), atol=1e-14)
     np.testing.assert_allclose(lse[0, 0], np.array(g["derived"]["lse"]), atol=1e-14)
+    # the page's explicit additive mask, no causal flag
+    m = np.array([[float(x) for x in row] for row in g["mask"]])[None, None]
+    o2, lse2 = oracle.attn_fwd(q, k, v, causal=False, scale=g["scale"], mask=m, lib=lib)
+    assert abs(o2[0, 0, 0, 0] - g["printed"]["o[0][0]"]) < g["printed"]["tolerance"]
+    np.testing.assert_allclose(o2[0, :, 0, :], np.array(g["derived"]["o"]), atol=1e-14)
+    np.testing.assert_allclose(lse2[0, 0], np.array(g["derived"]["lse"]), atol=1e-14)
 
 
 def pin_golden_decode_single_token(lib):
@@ -452,6 +458,37 @@ def pin_padded_head_dim(lib):
         np.testing.assert_allclose(op[..., :D], o, atol=1e-12)
         assert (op[..., D:] == 0).all()
         np.testing.assert_allclose(lsep, lse, atol=1e-12)
+
+
+def pin_additive_mask(lib):
+    """Additive masks: torch fp64 SDPA with a float attn_mask (broadcast over
+    batch, per head, and per batch and head; GQA); a mask of -inf above the
+    bottom-right diagonal equals causal=True; a constant mask c leaves O and
+    shifts the LSE by c."""
+    rng = np.random.default_rng(34)
+    B, Hq, Hkv, Sq, Skv, D = 2, 4, 2, 5, 9, 8
+    q, k, v = _rand(rng, B, Sq, Hq, D), _rand(rng, B, Skv, Hkv, D), _rand(rng, B, Skv, Hkv, D)
+    for shape in ((1, 1, Sq, Skv), (1, Hq, Sq, Skv), (B, Hq, Sq, Skv), (B, 1, Sq, Skv)):
+        m = rng.standard_normal(shape)
+        m[..., 1, 3] = -np.inf
+        o, lse = oracle.attn_fwd(q, k, v, scale=0.35, mask=m, lib=lib)
+        qt, kt, vt = (torch.tensor(_bshd(a)) for a in (q, k, v))
+        mt = torch.tensor(np.broadcast_to(m, (B, Hq, Sq, Skv)).copy())
+        ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mt, scale=0.35,
+                                             enable_gqa=True).permute(0, 2, 1, 3).numpy()
+        np.testing.assert_allclose(o, ref, atol=1e-12)
+        s = 0.35 * np.einsum("bihd,bjhd->bhij", q, np.repeat(k, Hq // Hkv, axis=2)) + \
+            np.broadcast_to(m, (B, Hq, Sq, Skv))
+        np.testing.assert_allclose(lse, scipy.special.logsumexp(s, axis=-1), atol=1e-12)
+    hide = np.where(np.arange(Skv)[None, :] > np.arange(Sq)[:, None] + (Skv - Sq), -np.inf, 0.0)
+    o1, l1 = oracle.attn_fwd(q, k, v, scale=0.35, mask=hide[None, None], lib=lib)
+    o2, l2 = oracle.attn_fwd(q, k, v, scale=0.35, causal=True, lib=lib)
+    np.testing.assert_allclose(o1, o2, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, atol=1e-14)
+    o3, l3 = oracle.attn_fwd(q, k, v, scale=0.35, mask=np.full((1, 1, Sq, Skv), 2.5), lib=lib)
+    o4, l4 = oracle.attn_fwd(q, k, v, scale=0.35, lib=lib)
+    np.testing.assert_allclose(o3, o4, atol=1e-13)
+    np.testing.assert_allclose(l3, l4 + 2.5, atol=1e-13)
 
 
 # ---------------------------------------------------------- backward --

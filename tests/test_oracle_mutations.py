@@ -4,7 +4,8 @@ Each mutation is a compile-time switch in oracle.c (ORACLE_MUTATION=n) that
 introduces one plausible slip: interleaved instead of contiguous GQA groups,
 top-left instead of bottom-right causal alignment, RoPE rotating the wrong way,
 K used in place of V, the scale dropped, a base-2 log in the LSE; in the
-backward, the D term, dK's scale, the inverse rotation, or the group sum.  The mutants
+backward, the D term, dK's scale, the inverse rotation, or the group sum; the
+additive mask scaled with the scores or read transposed.  The mutants
 are built into a temporary directory; the product oracle is untouched.
 """
 import os
@@ -26,6 +27,8 @@ MUTATIONS = {
     8: "backward without the scale on dK",
     9: "backward without the inverse rotation",
     10: "backward dK/dV from one query head of a group",
+    11: "additive mask multiplied by the scale",
+    12: "additive mask read transposed",
 }
 
 

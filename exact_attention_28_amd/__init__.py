@@ -8,6 +8,9 @@ on a GPU, the call raises.
 
 Entry points (same names as the C ABI):
   attn_fwd(q, k, v, causal=False, scale=None, rope_base=0.0, o=None, lse=None)
+  attn_fwd_masked(q, k, v, mask, causal=False, scale=None, rope_base=0.0, ...)
+  attn_bwd(q, k, v, o, dout, lse, causal=False, scale=None, rope_base=0.0, ...)
+  attn_prefill_kvcache(q, k_new, v_new, kcache, vcache, cache_lens, ...)
   attn_decode_splitkv(q, kcache, vcache, seqlens, num_splits, scale=None, ...)
   rope_apply(x, pos_offset=0, rope_base=10000.0)
   attn_decode_workspace_bytes(B, Hq, D, num_splits)
@@ -23,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_EMPTY_KV = 0, -1, -2, -3, -4
-EXPORTS = ("attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_decode_workspace_bytes",
+EXPORTS = ("attn_fwd", "attn_fwd_masked", "attn_bwd_workspace_bytes", "attn_bwd", "attn_decode_workspace_bytes",
            "attn_decode_splitkv", "attn_prefill_kvcache", "rope_apply", "attn_last_error")
 
 _lib = None
@@ -44,7 +47,11 @@ def load():
         raise ImportError(f"{LIB_PATH} is missing: build it with exact_attention_28_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    ll = ctypes.c_longlong
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, i, vp]
+    lib.attn_fwd_masked.argtypes = [vp, vp, vp, vp, ll, ll, ll, vp, vp, i, i, i, i, i, i, i, f, f,
+                                    i, vp]
+    lib.attn_fwd_masked.restype = i
     lib.attn_fwd.restype = i
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, f]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -121,6 +128,47 @@ def attn_fwd(q, k, v, causal=False, scale=None, rope_base=0.0, o=None, lse=None,
     _check(load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Skv, D,
                            int(bool(causal)), float(scale), float(rope_base), _dtype_code(q),
                            _stream(stream)))
+    return o, lse
+
+
+def attn_fwd_masked(q, k, v, mask, causal=False, scale=None, rope_base=0.0, o=None, lse=None,
+                    stream=None, want_lse=True):
+    """attn_fwd with an additive fp32 mask added to the scaled scores.
+
+    mask: fp32 tensor broadcastable to [B, Hq, Sq, Skv] (e.g. [Sq, Skv],
+    [B, 1, 1, Skv]); broadcast dimensions are passed as zero strides, so the
+    mask is never expanded in memory.  Its last dimension must be contiguous
+    (a mask whose last stride is not 1 is first made contiguous)."""
+    _need_gpu(q, k, v, o, lse)
+    if not mask.is_cuda:
+        raise ValueError("tensors must be on a GPU device")
+    B, Sq, Hq, D = q.shape
+    Bk, Skv, Hkv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if mask.dtype != torch.float32:
+        raise TypeError("mask must be fp32")
+    if mask.dim() > 4:
+        raise ValueError("mask has more than 4 dimensions")
+    if mask.dim() >= 1 and mask.shape[-1] > 1 and mask.stride(-1) != 1:
+        mask = mask.contiguous()
+    try:
+        m = mask.expand(B, Hq, Sq, Skv)
+    except RuntimeError as e:
+        raise ValueError(f"mask {tuple(mask.shape)} does not broadcast to "
+                         f"[{B}, {Hq}, {Sq}, {Skv}]") from e
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(load().attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(m), m.stride(0), m.stride(1),
+                                  m.stride(2), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Skv, D,
+                                  int(bool(causal)), float(scale), float(rope_base),
+                                  _dtype_code(q), _stream(stream)))
     return o, lse
 
 

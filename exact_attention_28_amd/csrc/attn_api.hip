@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <map>
@@ -97,7 +98,7 @@ int hip_status(hipError_t e, const char* what) {
 // width without rotation, then O's first D columns.
 int fwd_padded(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                int Hkv, int Sq, int Skv, int D, int causal, float scale, float rope_base,
-               int dtype, hipStream_t stream) {
+               int dtype, xattn::MaskView mask, hipStream_t stream) {
   const int Dp = D <= 64 ? 64 : 128;
   const size_t es = dtype == ATTN_BF16 ? 2 : 4;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -131,48 +132,44 @@ int fwd_padded(const void* q, const void* k, const void* v, void* o, float* lse,
     return hip_status(e, "attn_fwd: head-dim padding launch");
   if (dtype == ATTN_BF16)
     e = xattn::launch_fwd_bf16(qp, kp, vp, op, lse, B, Hq, Hkv, Sq, Skv, Dp, causal, scale,
-                               nullptr, stream);
+                               nullptr, stream, nullptr, 0, mask);
   else
     e = xattn::launch_fwd_f32(qp, kp, vp, op, lse, B, Hq, Hkv, Sq, Skv, Dp, causal, scale,
-                              nullptr, stream);
+                              nullptr, stream, mask);
   if (e != hipSuccess) return hip_status(e, "attn_fwd: kernel launch");
   e = xattn::launch_unpack_heads(op, o, (long long)B * Sq * Hq, D, Dp, dt, stream);
   return hip_status(e, "attn_fwd: head-dim unpadding launch");
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* attn_last_error(void) { return g_err.c_str(); }
-
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-             int Hkv, int Sq, int Skv, int D, int causal, float scale, float rope_base,
-             int dtype, hipStream_t stream) {
-  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID, "attn_fwd: null q, k, v or o");
-  if (Skv == 0) return fail(ATTN_ERR_EMPTY_KV, "attn_fwd: no keys (Skv == 0)");
+// attn_fwd and attn_fwd_masked (mask.p null: no mask); `fn` names the entry
+// point in error messages.
+int fwd(const char* fn, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+        int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale, float rope_base,
+        int dtype, xattn::MaskView mask, hipStream_t stream) {
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID, "%s: null q, k, v or o", fn);
+  if (Skv == 0) return fail(ATTN_ERR_EMPTY_KV, "%s: no keys (Skv == 0)", fn);
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1)
-    return fail(ATTN_ERR_INVALID, "attn_fwd: sizes must be >= 1 (B=%d Hq=%d Hkv=%d Sq=%d Skv=%d D=%d)",
-                B, Hq, Hkv, Sq, Skv, D);
+    return fail(ATTN_ERR_INVALID, "%s: sizes must be >= 1 (B=%d Hq=%d Hkv=%d Sq=%d Skv=%d D=%d)",
+                fn, B, Hq, Hkv, Sq, Skv, D);
   if (Hq % Hkv != 0)
-    return fail(ATTN_ERR_INVALID, "attn_fwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID, "attn_fwd: causal must be 0 or 1");
-  if (!finite_pos(scale)) return fail(ATTN_ERR_INVALID, "attn_fwd: scale must be finite and > 0");
+    return fail(ATTN_ERR_INVALID, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID, "%s: causal must be 0 or 1", fn);
+  if (!finite_pos(scale)) return fail(ATTN_ERR_INVALID, "%s: scale must be finite and > 0", fn);
   if (std::isnan(rope_base) || std::isinf(rope_base))
-    return fail(ATTN_ERR_INVALID, "attn_fwd: rope_base must be finite");
+    return fail(ATTN_ERR_INVALID, "%s: rope_base must be finite", fn);
   const bool rope = rope_base > 0.f;
-  if (rope && D % 2 != 0) return fail(ATTN_ERR_INVALID, "attn_fwd: RoPE needs an even head dim");
+  if (rope && D % 2 != 0) return fail(ATTN_ERR_INVALID, "%s: RoPE needs an even head dim", fn);
   if (dtype != ATTN_F32 && dtype != ATTN_BF16)
-    return fail(ATTN_ERR_INVALID, "attn_fwd: unknown dtype %d", dtype);
-  if (D > 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: D=%d (built: up to 128)", D);
+    return fail(ATTN_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (D > 128) return fail(ATTN_ERR_UNSUPPORTED, "%s: D=%d (built: up to 128)", fn, D);
   if (rope && Sq > Skv)
     return fail(ATTN_ERR_UNSUPPORTED,
-                "attn_fwd: RoPE with Sq > Skv would place queries at negative positions");
+                "%s: RoPE with Sq > Skv would place queries at negative positions", fn);
   if ((long long)B * Hq * ((Sq + 15) / 16) > 0x7fffffffLL || B > 65535 || Hq > 65535)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: grid too large");
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
   if (D != 64 && D != 128)
     return fwd_padded(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, rope_base, dtype,
-                      stream);
+                      mask, stream);
 
   const double2* tab = nullptr;
   const void* kin = k;
@@ -199,11 +196,42 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   hipError_t e;
   if (dtype == ATTN_BF16)
     e = xattn::launch_fwd_bf16(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab,
-                               stream);
+                               stream, nullptr, 0, mask);
   else
     e = xattn::launch_fwd_f32(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab,
-                              stream);
+                              stream, mask);
   return hip_status(e, "attn_fwd: kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int Sq, int Skv, int D, int causal, float scale, float rope_base,
+             int dtype, hipStream_t stream) {
+  return fwd("attn_fwd", q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, rope_base, dtype,
+             xattn::MaskView(), stream);
+}
+
+int attn_fwd_masked(const void* q, const void* k, const void* v, const float* mask,
+                    long long mask_bstride, long long mask_hstride, long long mask_rstride,
+                    void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                    int causal, float scale, float rope_base, int dtype, hipStream_t stream) {
+  if (!mask) return fail(ATTN_ERR_INVALID, "attn_fwd_masked: null mask");
+  if (mask_bstride < 0 || mask_hstride < 0 || mask_rstride < 0)
+    return fail(ATTN_ERR_INVALID, "attn_fwd_masked: mask strides must be >= 0");
+  xattn::MaskView m;
+  m.p = mask;
+  m.bs = mask_bstride;
+  m.hs = mask_hstride;
+  m.rs = mask_rstride;
+  m.vec = (reinterpret_cast<uintptr_t>(mask) % 16 == 0) && mask_bstride % 4 == 0 &&
+          mask_hstride % 4 == 0 && mask_rstride % 4 == 0;
+  return fwd("attn_fwd_masked", q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale,
+             rope_base, dtype, m, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D, float rope_base) {

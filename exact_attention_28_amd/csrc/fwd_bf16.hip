@@ -34,6 +34,11 @@
 //    rotation from the fp64 table, one rounding to bf16).  Keys are rotated
 //    once per call by the RoPE kernel before this one (each K tile is read by
 //    every query tile, so rotating it here would repeat the work Sq/128 times).
+//  * An additive mask (MASK) is read per lane as 16-byte chunks of 4 keys
+//    (the accumulator rows a lane holds come in runs of 4), issued at the top
+//    of each tile before the next tile's direct loads so that waiting for it
+//    never waits for the prefetch; it enters the scores as
+//    fma(s, scale * log2(e), mask * log2(e)).
 //  * Workgroups are issued heaviest-first under the causal mask, and the
 //    (batch, head group) index is the fastest-varying part of the block index
 //    so that the workgroups of one head group land on one XCD (block i runs on
@@ -74,12 +79,12 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buf
   }
 }
 
-template <int D, int HPW, bool CAUSAL, bool ROPE, int NQB>
+template <int D, int HPW, bool CAUSAL, bool ROPE, int NQB, bool MASK>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Skv_all,
     const int* __restrict__ kv_lens, int kv_rows, float scale_log2,
-    const double2* __restrict__ tab, int n_qt, int n_bh) {
+    const double2* __restrict__ tab, int n_qt, int n_bh, MaskView mask) {
   constexpr int BM = 128 * NQB, BN = 64, NP = BM / HPW;
   constexpr int KCH = D / 8;                 // 16-byte chunks per row
   constexpr int LD = BN * KCH / 256;         // 16-byte chunks per thread per tile (K and V each)
@@ -149,6 +154,16 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
       qf[qb][ks] = __builtin_bit_cast(bf16x8, wv);
     }
   }
+
+  // with a mask, the scores are scaled (and the mask added) right after the
+  // contraction, so the softmax below runs with unit scale
+  const float sl = MASK ? 1.f : scale_log2;
+  const float* mrow[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+    mrow[qb] = MASK ? mask.p + b * mask.bs + hh[qb] * mask.hs +
+                          (long long)(qvalid[qb] ? pos[qb] : 0) * mask.rs
+                    : nullptr;
 
   int kv_end = Skv;
   if (CAUSAL) kv_end = min(Skv, min(p0 + NP, Sq) - 1 + off + 1);
@@ -231,6 +246,34 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   // into (kn_, vn_), last read in the previous step, which every wave has left
   auto tile = [&](int t, const u16* kc_, const u16* vc_, u16* kn_, u16* vn_) {
     const int k0 = t * BN;
+    // mask values of this lane's 32 (query, key) pairs: keys
+    // k0 + 32 blk + 8a + 4g + e at accumulator row 4a + e; 0 past Skv.
+    // D = 64 issues them before the contraction (their latency hides behind
+    // it); D = 128 after it, where holding them across it would cost the
+    // registers of a second wave per SIMD.
+    float mv[NQB][2][16];
+    auto load_mask = [&]() {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int j0 = k0 + blk * 32 + 8 * a + 4 * g;
+            const float* mp = mrow[qb] + j0;
+            if (mask.vec && j0 + 4 <= Skv) {
+              const float4 x = *reinterpret_cast<const float4*>(mp);
+              mv[qb][blk][4 * a] = x.x;
+              mv[qb][blk][4 * a + 1] = x.y;
+              mv[qb][blk][4 * a + 2] = x.z;
+              mv[qb][blk][4 * a + 3] = x.w;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) mv[qb][blk][4 * a + e] = j0 + e < Skv ? mp[e] : 0.f;
+            }
+          }
+    };
+    if constexpr (MASK && D == 64) load_mask();
     if (t + 1 < ntiles) dma(k0 + BN, kn_, vn_);
 
     // S^T (64 keys x 32 queries per block) = K_tile Q^T
@@ -248,6 +291,17 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
         for (int qb = 0; qb < NQB; ++qb)
           s[qb][blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], s[qb][blk], 0, 0, 0);
       }
+    }
+
+    if constexpr (MASK) {
+      if constexpr (D != 64) load_mask();
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[qb][blk][r] = fmaf(s[qb][blk][r], scale_log2, mv[qb][blk][r] * kLog2e);
     }
 
     // mask: key rows past Skv, and keys after the query under the causal rule
@@ -278,7 +332,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                        false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const float mxs = mx * scale_log2;
+      const float mxs = mx * sl;
       if (__builtin_amdgcn_ballot_w64(mxs > m_run[qb] + 8.f)) {  // wave-uniform
         const float m_new = fmaxf(m_run[qb], mxs);
         const float alpha =
@@ -296,7 +350,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][blk][r], scale_log2, -m_use));
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][blk][r], sl, -m_use));
           s[qb][blk][r] = p;
           ls += p;
         }
@@ -358,65 +412,73 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   }
 }
 
-template <int D, int HPW, bool CAUSAL, bool ROPE, int NQB>
+template <int D, int HPW, bool CAUSAL, bool ROPE, int NQB, bool MASK>
 static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int Hq, int Hkv, int Sq, int Skv, const int* kv_lens, int kv_rows,
-                          float scale, const double2* tab, hipStream_t stream) {
+                          float scale, const double2* tab, MaskView mask, hipStream_t stream) {
   constexpr int NP = 128 * NQB / HPW;
   const int n_qt = (Sq + NP - 1) / NP;
   const int n_bh = B * (Hq / HPW);
   const long long nblocks = (long long)n_qt * n_bh;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  fwd_bf16_kernel<D, HPW, CAUSAL, ROPE, NQB><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
-      static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v),
-      static_cast<u16*>(o), lse, Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale * kLog2e, tab, n_qt,
-      n_bh);
+  fwd_bf16_kernel<D, HPW, CAUSAL, ROPE, NQB, MASK>
+      <<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
+          static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v),
+          static_cast<u16*>(o), lse, Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale * kLog2e, tab,
+          n_qt, n_bh, mask);
   return hipGetLastError();
 }
 
 // Two query blocks per wave halve the LDS traffic per MFMA (D = 64, where the
 // registers allow it); one block keeps small problems spread over more
-// workgroups (at least two per CU).
+// workgroups (at least two per CU).  Masked runs use one block (the mask
+// values take the registers a second block would need).
 template <int D, int HPW, bool CAUSAL, bool ROPE>
 static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int Hq, int Hkv, int Sq, int Skv, const int* kv_lens, int kv_rows,
-                          float scale, const double2* tab, hipStream_t stream) {
-  const long long wg2 = (long long)((Sq + 256 / HPW - 1) / (256 / HPW)) * B * (Hq / HPW);
-  if (D == 64 && wg2 >= 2 * 256)
-    return go_bf16<D, HPW, CAUSAL, ROPE, 2>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
-                                            kv_rows, scale, tab, stream);
-  return go_bf16<D, HPW, CAUSAL, ROPE, 1>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
-                                          scale, tab, stream);
+                          float scale, const double2* tab, MaskView mask, hipStream_t stream) {
+  if (mask.p != nullptr)
+    return go_bf16<D, HPW, CAUSAL, ROPE, 1, true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
+                                                  kv_rows, scale, tab, mask, stream);
+  if constexpr (D == 64) {
+    const long long wg2 = (long long)((Sq + 256 / HPW - 1) / (256 / HPW)) * B * (Hq / HPW);
+    if (wg2 >= 2 * 256)
+      return go_bf16<D, HPW, CAUSAL, ROPE, 2, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv,
+                                                     kv_lens, kv_rows, scale, tab, mask, stream);
+  }
+  return go_bf16<D, HPW, CAUSAL, ROPE, 1, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
+                                                 kv_rows, scale, tab, mask, stream);
 }
 
 template <int D, bool CAUSAL, bool ROPE>
 static hipError_t pick_hpw(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Sq, int Skv, const int* kv_lens,
-                           int kv_rows, float scale, const double2* tab, hipStream_t stream) {
+                           int kv_rows, float scale, const double2* tab, MaskView mask,
+                           hipStream_t stream) {
   const int G = Hq / Hkv;
   if (G % 8 == 0)
     return go_bf16<D, 8, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
-                                       scale, tab, stream);
+                                       scale, tab, mask, stream);
   if (G % 4 == 0)
     return go_bf16<D, 4, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
-                                       scale, tab, stream);
+                                       scale, tab, mask, stream);
   if (G % 2 == 0)
     return go_bf16<D, 2, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
-                                       scale, tab, stream);
+                                       scale, tab, mask, stream);
   return go_bf16<D, 1, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
-                                     scale, tab, stream);
+                                     scale, tab, mask, stream);
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
                            float scale, const double2* rope_tab, hipStream_t stream,
-                           const int* kv_lens, int kv_rows) {
+                           const int* kv_lens, int kv_rows, MaskView mask) {
   const bool rope = rope_tab != nullptr;
   if (kv_lens == nullptr) kv_rows = Skv;
 #define XATTN_BF16_CASE(DD, C, R)                                                          \
   if (D == DD && (causal != 0) == C && rope == R)                                        \
     return pick_hpw<DD, C, R>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale, \
-                              rope_tab, stream);
+                              rope_tab, mask, stream);
   XATTN_BF16_CASE(64, false, false)
   XATTN_BF16_CASE(64, true, false)
   XATTN_BF16_CASE(64, false, true)

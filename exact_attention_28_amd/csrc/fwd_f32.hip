@@ -18,7 +18,7 @@ template <int D, bool CAUSAL, bool ROPE>
 __global__ __launch_bounds__(128) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Skv,
-    float scale_log2, const double2* __restrict__ tab) {
+    float scale_log2, const double2* __restrict__ tab, MaskView mask) {
   constexpr int BQ = 64;
   constexpr int BK = (D == 64) ? 64 : 32;
   constexpr int HD = D / 2;
@@ -53,6 +53,9 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(
     for (int d = 0; d < HD; ++d) o[d] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
+  // this row's additive mask (the [WH] compute_block_scores mask term), or null
+  const float* mrow =
+      mask.p ? mask.p + b * mask.bs + h * mask.hs + (long long)(i < Sq ? i : 0) * mask.rs : nullptr;
 
   int kv_end = Skv;
   if (CAUSAL) {
@@ -90,8 +93,10 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(
       float part = 0.f;
 #pragma unroll
       for (int d = 0; d < HD; ++d) part = fmaf(q[d], Ks[jj][half * HD + d], part);
-      float x = (part + __shfl_xor(part, 1)) * scale_log2;
       const int j = k0 + jj;
+      const float dot = part + __shfl_xor(part, 1);
+      float x = dot * scale_log2;
+      if (mrow != nullptr && j < Skv) x = fmaf(dot, scale_log2, mrow[j] * kLog2e);
       if (j >= Skv || (CAUSAL && j > i + off)) x = -INFINITY;
       s[jj] = x;
       bmax = fmaxf(bmax, x);
@@ -125,21 +130,21 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(
 template <int D, bool CAUSAL, bool ROPE>
 static hipError_t go_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                          int Hq, int Hkv, int Sq, int Skv, float scale, const double2* tab,
-                         hipStream_t stream) {
+                         MaskView mask, hipStream_t stream) {
   dim3 grid((Sq + 63) / 64, Hq, B);
   fwd_f32_kernel<D, CAUSAL, ROPE><<<grid, dim3(128), 0, stream>>>(
       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-      static_cast<float*>(o), lse, Hq, Hkv, Sq, Skv, scale * kLog2e, tab);
+      static_cast<float*>(o), lse, Hq, Hkv, Sq, Skv, scale * kLog2e, tab, mask);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
-                          const double2* rope_tab, hipStream_t stream) {
+                          const double2* rope_tab, hipStream_t stream, MaskView mask) {
   const bool rope = rope_tab != nullptr;
 #define XATTN_F32_CASE(DD, C, R)                                                           \
   if (D == DD && (causal != 0) == C && rope == R)                                        \
-    return go_f32<DD, C, R>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, rope_tab, stream);
+    return go_f32<DD, C, R>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, rope_tab, mask, stream);
   XATTN_F32_CASE(64, false, false)
   XATTN_F32_CASE(64, true, false)
   XATTN_F32_CASE(64, false, true)

@@ -6,17 +6,29 @@
 
 namespace xattn {
 
+// Additive fp32 mask for the forward: element (b, h, i, j) at
+// p[b*bs + h*hs + i*rs + j] (strides in elements; 0 broadcasts), added to the
+// scaled score of query row i and key j of batch b, query head h.  vec: p and
+// the strides allow 16-byte loads (p 16-byte aligned, strides multiples of 4).
+struct MaskView {
+  const float* p = nullptr;
+  long long bs = 0, hs = 0, rs = 0;
+  bool vec = false;
+};
+
 // Prefill: q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D], o like q, lse [B,Hq,Sq] (nullable).
 // rope_tab: table rows for positions [0, Skv); query row i uses row Skv-Sq+i.
 // bf16 rotates only the queries in the kernel (keys arrive rotated); fp32
 // rotates queries and keys.  Null disables rotation.
 // bf16 with kv_lens non-null: k/v are caches of kv_rows rows per batch and
 // batch b attends to its first min(kv_lens[b], kv_rows - Sq) + Sq rows (Skv
-// is then unused; the table must cover kv_rows positions).
+// is then unused; the table must cover kv_rows positions).  mask.p non-null
+// adds the mask to the scores (bf16 and fp32).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
                            float scale, const double2* rope_tab, hipStream_t stream,
-                           const int* kv_lens = nullptr, int kv_rows = 0);
+                           const int* kv_lens = nullptr, int kv_rows = 0,
+                           MaskView mask = MaskView());
 
 // Cache append: rows t < Sq of k_new/v_new [B,Sq,Hkv,D] (bf16) go to rows
 // L_b + t of kcache/vcache [B,rows,Hkv,D] with L_b = min(max(lens[b], 0),
@@ -27,7 +39,8 @@ hipError_t launch_cache_append(const void* k_new, const void* v_new, void* kcach
                                const double2* tab, hipStream_t stream);
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                           int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
-                          float scale, const double2* rope_tab, hipStream_t stream);
+                          float scale, const double2* rope_tab, hipStream_t stream,
+                          MaskView mask = MaskView());
 
 // RoPE: row t of the table holds (cos, sin)((pos0 + t) / base^(2i/D)) for
 // t < npos, i < D/2, in fp64.

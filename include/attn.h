@@ -97,6 +97,30 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              int dtype, hipStream_t stream);
 
 /*
+ * attn_fwd_masked — attn_fwd with an additive float mask on the scores.
+ *
+ * As attn_fwd, with the score of query row i and key j of batch b, head h
+ *   s_ij = scale * <q~[b,i,h,:], k~[b,j,g,:]> + mask[b*mask_bstride +
+ *          h*mask_hstride + i*mask_rstride + j]
+ * (the mask term of [WH] compute_block_scores, added to the scaled dot
+ * product; the attn_mask of scaled_dot_product_attention), then the causal
+ * rule and the softmax as in attn_fwd.  The mask is an fp32 device array owned
+ * by the caller; strides are in elements and may be 0 to broadcast (e.g.
+ * mask_bstride = mask_hstride = 0 for one [Sq, Skv] mask shared by every batch
+ * and head, mask_rstride = 0 for a per-key padding mask); the columns j are
+ * contiguous.  Entries must be finite or -inf: -inf hides a key, and a row
+ * whose keys are all hidden gets O = 0 and lse = -inf.  Every address
+ * b*mask_bstride + h*mask_hstride + i*mask_rstride + j (b < B, h < Hq, i < Sq,
+ * j < Skv) must lie in the array.
+ * Errors: as attn_fwd, and ATTN_ERR_INVALID for a null mask or a negative
+ *   stride.
+ */
+int attn_fwd_masked(const void* q, const void* k, const void* v, const float* mask,
+                    long long mask_bstride, long long mask_hstride, long long mask_rstride,
+                    void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                    int causal, float scale, float rope_base, int dtype, hipStream_t stream);
+
+/*
  * attn_bwd_workspace_bytes — size of the workspace attn_bwd needs: the per-row
  * D_i and log2 lse ([B, Hq, Sq] fp32 each) and, with rope_base > 0, the rotated
  * Q and K (B*Sq*Hq*D and B*Skv*Hkv*D bf16), each part rounded up to 256 bytes.

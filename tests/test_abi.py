@@ -65,6 +65,39 @@ def test_attn_fwd_validation(lib, kw, code):
     assert xa.last_error() != ""
 
 
+def _fwdm(lib, mask=FAKE, bs=0, hs=0, rs=8, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=4, Hkv=2, Sq=8, Skv=8, D=64,
+             causal=0, scale=0.125, rope=0.0, dtype=1)
+    a.update(kw)
+    return lib.attn_fwd_masked(a["q"], a["k"], a["v"], mask, bs, hs, rs, a["o"], a["lse"], a["B"],
+                               a["Hq"], a["Hkv"], a["Sq"], a["Skv"], a["D"], a["causal"],
+                               a["scale"], a["rope"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), xa.ATTN_ERR_INVALID),
+    (dict(bs=-1), xa.ATTN_ERR_INVALID),
+    (dict(hs=-64), xa.ATTN_ERR_INVALID),
+    (dict(rs=-8), xa.ATTN_ERR_INVALID),
+    (dict(q=None), xa.ATTN_ERR_INVALID),
+    (dict(Skv=0), xa.ATTN_ERR_EMPTY_KV),
+    (dict(Hq=6, Hkv=4), xa.ATTN_ERR_INVALID),
+    (dict(scale=0.0), xa.ATTN_ERR_INVALID),
+    (dict(D=256), xa.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=5), xa.ATTN_ERR_INVALID),
+])
+def test_attn_fwd_masked_validation(lib, kw, code):
+    assert _fwdm(lib, **kw) == code
+    assert "attn_fwd_masked" in xa.last_error()
+
+
+def test_attn_fwd_masked_binding_checks():
+    import torch
+    q = torch.zeros(1, 4, 2, 64)
+    with pytest.raises(ValueError):  # CPU tensors are refused before any call
+        xa.attn_fwd_masked(q, q, q, torch.zeros(4, 4))
+
+
 def _dec(lib, q=FAKE, kc=FAKE, vc=FAKE, sl=FAKE, o=FAKE, B=2, Hq=8, Hkv=2, D=128, ns=4,
          scale=0.088, smax=64):
     return lib.attn_decode_splitkv(q, kc, vc, sl, o, B, Hq, Hkv, D, ns, scale, smax, None, None,

@@ -1,0 +1,179 @@
+"""GPU parity of the forward with an additive float mask (attn_fwd_masked
+through the C ABI) against the fp64 oracle given the same fp32 mask values.
+
+The bars are those of the unmasked forward (bf16: O max-abs 2e-2, rel-L2
+5e-3, LSE max-abs 1e-3; fp32: 1e-4).  Masks are standard normal values times
+2 with about a tenth of the entries -inf; they are passed in every broadcast
+form the entry point takes (one [Sq, Skv] mask, per head, per batch and head,
+a per-key padding row), with row lengths that do and do not allow 16-byte
+loads, together with the causal flag, RoPE, grouped heads and padded head
+dims.  Rows whose keys are all hidden give O = 0 and lse = -inf.
+"""
+import json
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_28_amd as xa
+import oracle
+import workloads as W
+from test_gpu_parity import check_bf16, check_f32
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _mask(rng, shape, hide=0.1):
+    m = (rng.standard_normal(shape) * 2.0).astype(np.float32)
+    m[rng.random(shape) < hide] = -np.inf
+    return m
+
+
+def run_masked(q, k, v, mask, causal, scale, rope):
+    o, lse = xa.attn_fwd_masked(W.to_device(q), W.to_device(k), W.to_device(v),
+                                torch.from_numpy(mask).to("cuda"), causal=causal, scale=scale,
+                                rope_base=rope)
+    torch.cuda.synchronize()
+    return _np(o), _np(lse)
+
+
+def _oracle(q, k, v, mask, causal, scale, rope, B, Hq, Sq, Skv, **kw):
+    """The oracle takes a [1 or B, 1 or Hq, Sq, Skv] mask: a mask broadcast over
+    query rows is widened along that axis first."""
+    m4 = mask.reshape((1,) * (4 - mask.ndim) + mask.shape).astype(np.float64)
+    m4 = np.broadcast_to(m4, (m4.shape[0], m4.shape[1], Sq, Skv))
+    return oracle.attn_fwd(q, k, v, causal=causal, scale=scale, rope_base=rope, mask=m4,
+                           nthreads=NTHREADS, **kw)
+
+
+def test_golden_explicit_mask():
+    """The page's two-token example with its explicit [[0, -inf], [0, 0]] mask
+    (head dim 4, through the padded path): output[0] = 1.0, and the derived
+    O and LSE."""
+    g = json.load(open(os.path.join(GOLDEN, "whisper_causal_mask_example.json")))
+    mask = np.array([[float(x) for x in r] for r in g["mask"]], dtype=np.float32)
+    for dt in ("f32", "bf16"):
+        say("case golden mask", dt)
+        q, k, v = (np.array(g[n], dtype=np.float32)[None, :, None, :] for n in ("q", "k", "v"))
+        if dt == "bf16":
+            q, k, v = (W.f32_to_bf16_bits(x) for x in (q, k, v))
+        o, lse = run_masked(q, k, v, mask, False, g["scale"], 0.0)
+        assert abs(o[0, 0, 0, 0] - g["printed"]["o[0][0]"]) < g["printed"]["tolerance"]
+        np.testing.assert_allclose(o[0, :, 0, :], np.array(g["derived"]["o"]), atol=1e-6)
+        np.testing.assert_allclose(lse[0, 0], np.array(g["derived"]["lse"]), atol=1e-6)
+
+
+MASK_CASES = [  # B, Hq, Hkv, Sq, Skv, D, causal, rope, mask shape ('s' [Sq,Skv], 'h', 'bh', 'kp')
+    (2, 8, 2, 200, 333, 64, False, 0.0, "s"),      # ragged keys: scalar mask loads
+    (2, 8, 2, 256, 256, 64, True, 10000.0, "bh"),  # 16-byte loads, causal, RoPE
+    (1, 4, 4, 130, 300, 128, True, 0.0, "h"),      # D = 128, per-head mask
+    (3, 6, 3, 97, 160, 64, False, 500.0, "kp"),    # per-key padding row [B,1,1,Skv]
+    (1, 16, 2, 129, 129, 128, False, 10000.0, "s"),  # 8 heads per kv head
+    (1, 3, 3, 64, 64, 64, True, 0.0, "bh"),        # one tile
+    (2, 4, 1, 1, 517, 64, False, 0.0, "bh"),       # one query row
+    (1, 4, 2, 50, 90, 40, True, 10000.0, "s"),     # padded head dim
+]
+
+
+def _mask_shape(kind, B, Hq, Sq, Skv):
+    return {"s": (Sq, Skv), "h": (1, Hq, Sq, Skv), "bh": (B, Hq, Sq, Skv),
+            "kp": (B, 1, 1, Skv)}[kind]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=[str(c) for c in MASK_CASES])
+def test_masked_bf16(case):
+    B, Hq, Hkv, Sq, Skv, D, causal, rope, kind = case
+    say("case mask bf16", case)
+    rng = np.random.default_rng(abs(hash(case)) % 2 ** 32)
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, Sq, Hq, D), dtype=np.float32))
+    k = W.f32_to_bf16_bits(rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32))
+    v = W.f32_to_bf16_bits(rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32))
+    mask = _mask(rng, _mask_shape(kind, B, Hq, Sq, Skv))
+    scale = float(np.float32(1 / math.sqrt(D)))
+    o, lse = run_masked(q, k, v, mask, causal, scale, rope)
+    o_ref, lse_ref = _oracle(q, k, v, mask, causal, scale, rope, B, Hq, Sq, Skv)
+    check_bf16(o, lse, o_ref, lse_ref, f"mask {case}")
+
+
+@pytest.mark.parametrize("case", [(2, 4, 2, 100, 150, 64, True, 0.0, "bh"),
+                                  (1, 2, 1, 33, 70, 128, False, 10000.0, "s"),
+                                  (2, 2, 2, 45, 80, 24, False, 0.0, "kp")],
+                         ids=str)
+def test_masked_f32(case):
+    B, Hq, Hkv, Sq, Skv, D, causal, rope, kind = case
+    say("case mask f32", case)
+    rng = np.random.default_rng(abs(hash(case)) % 2 ** 32)
+    q = rng.standard_normal((B, Sq, Hq, D), dtype=np.float32)
+    k = rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32)
+    v = rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32)
+    mask = _mask(rng, _mask_shape(kind, B, Hq, Sq, Skv))
+    scale = float(np.float32(1 / math.sqrt(D)))
+    o, lse = run_masked(q, k, v, mask, causal, scale, rope)
+    o_ref, lse_ref = _oracle(q, k, v, mask, causal, scale, rope, B, Hq, Sq, Skv)
+    check_f32(o, lse, o_ref, lse_ref, f"mask f32 {case}")
+
+
+def test_fully_hidden_rows_and_strided_mask():
+    """Rows whose keys are all -inf give O = 0 and lse = -inf; a mask that is a
+    strided view (rows of a wider array, a row pitch that rules out 16-byte
+    loads) and one broadcast by expand() give the same bits as their contiguous
+    copies."""
+    B, Hq, Hkv, Sq, Skv, D = 2, 4, 2, 70, 100, 64
+    rng = np.random.default_rng(11)
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, Sq, Hq, D), dtype=np.float32))
+    k = W.f32_to_bf16_bits(rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32))
+    v = W.f32_to_bf16_bits(rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32))
+    mask = _mask(rng, (Sq, Skv))
+    mask[[0, 5, 69]] = -np.inf
+    o, lse = run_masked(q, k, v, mask, False, 0.125, 0.0)
+    assert (o[:, [0, 5, 69]] == 0).all() and (lse[:, :, [0, 5, 69]] == -np.inf).all()
+    o_ref, lse_ref = _oracle(q, k, v, mask, False, 0.125, 0.0, B, Hq, Sq, Skv)
+    check_bf16(o, lse, o_ref, lse_ref, "hidden rows")
+    qd, kd, vd = W.to_device(q), W.to_device(k), W.to_device(v)
+    wide = torch.zeros(Sq, Skv + 27, device="cuda")
+    wide[:, :Skv] = torch.from_numpy(mask).cuda()
+    a, la = xa.attn_fwd_masked(qd, kd, vd, wide[:, :Skv], scale=0.125)
+    b, lb = xa.attn_fwd_masked(qd, kd, vd, wide[:, :Skv].contiguous(), scale=0.125)
+    c, lc = xa.attn_fwd_masked(qd, kd, vd, wide[:, :Skv].contiguous().expand(B, Hq, Sq, Skv),
+                               scale=0.125)
+    torch.cuda.synchronize()
+    for x, y in ((a, b), (a, c)):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(la, lb) and torch.equal(la, lc)
+
+
+def test_lfm2_workload_with_mask_sampled():
+    """The LFM2 prefill workload (B4 Hq32 Hkv8 S4096 D64, causal, RoPE) with a
+    shared [4096, 4096] mask (a 1024-key sliding window plus random -inf and
+    normal entries inside it), sampled rows of every (batch, head)."""
+    cfg = W.C4
+    say("case", cfg.name, "masked")
+    q, k, v = W.prefill_inputs(cfg)
+    rng = np.random.default_rng(cfg.seed + 13)
+    S = cfg.Sq
+    mask = _mask(rng, (S, S), hide=0.05)
+    i, j = np.arange(S)[:, None], np.arange(S)[None, :]
+    mask[j < i - 1023] = -np.inf
+    o, lse = run_masked(q, k, v, mask, cfg.causal, cfg.scale, cfg.rope_base)
+    rows = sorted(set([0, 1, 63, 64, 1023, 1024, 1025, S - 1] +
+                      [int(r) for r in rng.choice(S, 24, replace=False)]))
+    o_ref, lse_ref = _oracle(q, k, v, mask, cfg.causal, cfg.scale, cfg.rope_base, cfg.B, cfg.Hq,
+                             S, S, rows=rows, units=list(range(cfg.B * cfg.Hq)))
+    # o: [B,Sq,Hq,D] -> [unit, row, D];  lse: [B,Hq,Sq] -> [unit, row]
+    og = o[:, rows].transpose(0, 2, 1, 3).reshape(cfg.B * cfg.Hq, len(rows), cfg.D)
+    lg = lse[:, :, rows].reshape(cfg.B * cfg.Hq, len(rows))
+    check_bf16(og, lg, o_ref, lse_ref, f"{cfg.name} masked")

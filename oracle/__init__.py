@@ -6,8 +6,9 @@ calls it, and it imports nothing from the HIP library.
 
 This module only marshals numpy arrays into ``liboracle.so`` (compiled from
 ``oracle.c`` by ``oracle/build.py``); every step of the arithmetic is in
-``oracle.c``.  Inputs may be float64, float32, or uint16 arrays holding bf16
-bit patterns; they are widened exactly inside the oracle.
+``oracle.c``.  Inputs may be float64, float32, float16 (IEEE binary16), or
+uint16 arrays holding bf16 bit patterns; they are widened exactly inside the
+oracle.
 """
 import ctypes
 import os
@@ -19,8 +20,8 @@ from . import build as _build
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
 
-F64, F32, BF16 = 0, 1, 2
-ROUND_NONE, ROUND_BF16, ROUND_F32 = 0, 8, 24
+F64, F32, BF16, F16 = 0, 1, 2, 3
+ROUND_NONE, ROUND_BF16, ROUND_F16, ROUND_F32 = 0, 8, 11, 24
 
 _dp = ctypes.POINTER(ctypes.c_double)
 _ip = ctypes.POINTER(ctypes.c_int)
@@ -72,6 +73,8 @@ def _as_input(x):
         return x, F32
     if x.dtype in (np.uint16, np.int16):
         return x.view(np.uint16), BF16
+    if x.dtype == np.float16:
+        return x.view(np.uint16), F16
     raise TypeError(f"unsupported oracle input dtype {x.dtype}")
 
 
@@ -91,7 +94,7 @@ def _ints(seq):
 
 
 def default_round_bits(dtype_code):
-    return {F64: ROUND_NONE, F32: ROUND_F32, BF16: ROUND_BF16}[dtype_code]
+    return {F64: ROUND_NONE, F32: ROUND_F32, BF16: ROUND_BF16, F16: ROUND_F16}[dtype_code]
 
 
 def attn_fwd(q, k, v, causal=False, scale=None, rope_base=0.0, round_bits=None, rows=None,

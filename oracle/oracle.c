@@ -13,8 +13,8 @@
  *   [FD]  oxibonsai-model 0.1.4, src/layers/flash_decode.rs
  *   [LF]  whisper-apr 0.3.1, src/model/lfm2/gqa.rs
  *
- * Everything is computed in fp64.  Inputs may be given as fp64, fp32 or bf16 bit
- * patterns; they are widened exactly to fp64 on access.  The score matrix of
+ * Everything is computed in fp64.  Inputs may be given as fp64, fp32, bf16 or
+ * IEEE binary16 (fp16) bit patterns; they are widened exactly to fp64 on access.  The score matrix of
  * every (batch, query head) is materialised in full before the softmax, as in the
  * naive path of [WH] (fn scaled_dot_product_attention of MultiHeadAttention) and
  * the scalar path of [LF] (fn attention_scalar).
@@ -45,6 +45,7 @@
 #define ORC_F64 0
 #define ORC_F32 1
 #define ORC_BF16 2
+#define ORC_F16 3
 
 #ifdef ORACLE_MUTATION
 /* Planted mistakes, compiled only by the mutation test: each one is a plausible
@@ -59,6 +60,25 @@
 static double widen(const void* p, int dtype, size_t idx) {
   if (dtype == ORC_F64) return ((const double*)p)[idx];
   if (dtype == ORC_F32) return (double)((const float*)p)[idx];
+  if (dtype == ORC_F16) {
+    /* IEEE 754 binary16: sign, 5 exponent bits (bias 15), 10 fraction bits;
+     * exponent 0 holds zero and the subnormals (fraction * 2^-24), exponent 31
+     * infinities and NaNs */
+    const uint16_t h = ((const uint16_t*)p)[idx];
+    const int sgn = h >> 15, ex = (h >> 10) & 31, fr = h & 1023;
+    double v;
+    if (ex == 0)
+      v = ldexp((double)fr, -24);
+    else if (ex == 31)
+      v = fr ? NAN : INFINITY;
+    else
+#if MUT == 13
+      v = ldexp((double)(1024 + fr), ex - 24); /* planted: exponent bias 14 */
+#else
+      v = ldexp((double)(1024 + fr), ex - 25);
+#endif
+    return sgn ? -v : v;
+  }
   /* bf16: the 16 stored bits are the top half of an IEEE binary32 */
   uint32_t bits = (uint32_t)((const uint16_t*)p)[idx] << 16;
   float f;
@@ -67,14 +87,23 @@ static double widen(const void* p, int dtype, size_t idx) {
 }
 
 /* Nearest value with `sig` significant bits, ties to even (sig = 8 for bf16,
- * 24 for binary32; 0 = keep fp64).  Exponent-range limits are ignored: the
- * values here are far from overflow and from subnormals. */
+ * 24 for binary32; 0 = keep fp64).  For bf16 and binary32 the exponent-range
+ * limits are ignored: the values here are far from overflow and from their
+ * subnormals.  sig = 11 is IEEE binary16, whose range is narrow enough to
+ * matter: below 2^-14 (the subnormals) the spacing is fixed at 2^-24, and a
+ * value that rounds to 2^16 or more (|x| >= 65520) becomes an infinity. */
 double oracle_round_sig(double x, int sig) {
   if (sig <= 0 || x == 0.0 || !isfinite(x)) return x;
+#if MUT != 14
+  if (sig == 11 && fabs(x) < ldexp(1.0, -14))
+    return ldexp(nearbyint(ldexp(x, 24)), -24);
+#endif
   int e;
   double m = frexp(x, &e);            /* x = m * 2^e, 0.5 <= |m| < 1 */
   double r = nearbyint(ldexp(m, sig)); /* default rounding: nearest, ties even */
-  return ldexp(r, e - sig);
+  double y = ldexp(r, e - sig);
+  if (sig == 11 && fabs(y) > 65504.0) return x > 0 ? INFINITY : -INFINITY;
+  return y;
 }
 
 /* ------------------------------------------------------------------ RoPE -- */

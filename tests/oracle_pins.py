@@ -5,7 +5,7 @@ when the oracle disagrees with:
   * values the pages print for a worked example (fixtures in tests/golden/),
   * a library routine the definition reduces to (torch's fp64 CPU
     scaled_dot_product_attention, scipy's logsumexp, numpy complex arithmetic,
-    numpy's binary32 rounding, torch's bfloat16 rounding),
+    numpy's binary32 and binary16 rounding, torch's bfloat16 rounding),
   * closed forms and invariants of the mathematics.
 The same functions run against deliberately broken builds of the oracle in
 test_oracle_mutations.py, which checks that every planted mistake is caught.
@@ -167,6 +167,41 @@ def pin_rounding(lib):
     assert oracle.round_sig(1.0 + 2.0 ** -8, 8, lib=lib) == 1.0
     assert oracle.round_sig(1.0 + 3 * 2.0 ** -8, 8, lib=lib) == 1.0 + 2.0 ** -6
     assert oracle.round_sig(-(1.0 + 3 * 2.0 ** -8), 8, lib=lib) == -(1.0 + 2.0 ** -6)
+
+
+def pin_f16(lib):
+    """IEEE binary16 inputs and rounding: every finite bit pattern widens to
+    numpy's float16 value (and a few to the values of the format's definition);
+    rounding to 11 bits equals numpy's direct float64 -> float16 conversion,
+    subnormals and overflow included, with hand-checked ties."""
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    pats = pats[((pats >> 10) & 31) != 31]                 # finite patterns only
+    x16 = pats.view(np.float16).reshape(1, 1, -1, 64)
+    # position 0 rotates by angle 0: the widened inputs come back unchanged
+    w = oracle.rope(x16, 0, 10000.0, round_bits=0, lib=lib)
+    np.testing.assert_array_equal(w.ravel(), x16.astype(np.float64).ravel())
+    byp = dict(zip(pats.tolist(), w.ravel().tolist()))
+    for bitsv, val in ((0x0001, 2.0 ** -24), (0x03FF, 1023 * 2.0 ** -24), (0x0400, 2.0 ** -14),
+                       (0x3C00, 1.0), (0x3C01, 1.0 + 2.0 ** -10), (0xC000, -2.0),
+                       (0x7BFF, 65504.0), (0x3555, 0.333251953125)):
+        assert byp[bitsv] == val, (hex(bitsv), byp[bitsv], val)
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal(3000) * 2.0 ** rng.integers(-30, 18, 3000).astype(np.float64)
+    for xi in x:
+        assert oracle.round_sig(xi, 11, lib=lib) == float(np.float16(xi)), xi
+    for xi, want in ((1.0 + 2.0 ** -11, 1.0), (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),
+                     (2.0 ** -25, 0.0), (3 * 2.0 ** -25, 2.0 ** -23), (1.5 * 2.0 ** -24, 2.0 ** -23),
+                     (65519.0, 65504.0), (65520.0, np.inf), (-65520.0, -np.inf)):
+        assert oracle.round_sig(xi, 11, lib=lib) == want, (xi, want)
+    # attention on fp16 inputs with RoPE: the rotated q, k rounded to fp16
+    f = [rng.standard_normal(sh).astype(np.float16) for sh in ((1, 7, 2, 16), (1, 7, 1, 16),
+                                                                (1, 7, 1, 16))]
+    o, lse = oracle.attn_fwd(*f, causal=True, scale=0.25, rope_base=10000.0, lib=lib)
+    q, k, v = (a.astype(np.float64) for a in f)
+    qr = _rope_complex(q, 0, 10000.0).astype(np.float16).astype(np.float64)
+    kr = _rope_complex(k, 0, 10000.0).astype(np.float16).astype(np.float64)
+    np.testing.assert_allclose(o, _torch_sdpa(qr, kr, v, True, 0.25), atol=1e-12)
+    np.testing.assert_allclose(lse, _scipy_lse(qr, kr, True, 0.25), atol=1e-12)
 
 
 # ---------------------------------------------------------- RoPE --

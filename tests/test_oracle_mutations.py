@@ -5,7 +5,8 @@ introduces one plausible slip: interleaved instead of contiguous GQA groups,
 top-left instead of bottom-right causal alignment, RoPE rotating the wrong way,
 K used in place of V, the scale dropped, a base-2 log in the LSE; in the
 backward, the D term, dK's scale, the inverse rotation, or the group sum; the
-additive mask scaled with the scores or read transposed.  The mutants
+additive mask scaled with the scores or read transposed; fp16 decoded with a
+wrong exponent bias or rounded without its subnormal range.  The mutants
 are built into a temporary directory; the product oracle is untouched.
 """
 import os
@@ -29,6 +30,8 @@ MUTATIONS = {
     10: "backward dK/dV from one query head of a group",
     11: "additive mask multiplied by the scale",
     12: "additive mask read transposed",
+    13: "fp16 exponent bias 14",
+    14: "fp16 rounding without its subnormal range",
 }
 
 

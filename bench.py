@@ -35,8 +35,8 @@ import workloads as W  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 METRIC = "attention fwd TFLOP/s + decode KV GB/s, as % of MI355X MFMA/HBM peak"
-KERNEL_SOURCES = ("fwd_bf16.hip", "common.h", "lds.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_lfm2_gqa_prefill_s4096_traffic.txt")
+KERNEL_SOURCES = ("fwd16.hip", "common.h", "lds.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd16_lfm2_gqa_prefill_s4096_traffic.txt")
 
 
 def log(*a):
@@ -160,7 +160,7 @@ def traffic_summary(fetch_csv, write_csv, out_path, cmds):
                 continue
             name = r["Kernel_Name"]
             is_copy = "elementwise" in name and "add" in name.lower()  # not the fill of src
-            key = "attn" if "fwd_bf16_kernel" in name else ("copy" if is_copy else None)
+            key = "attn" if "fwd16_kernel" in name else ("copy" if is_copy else None)
             if key:
                 vals[key].append(float(r["Counter_Value"]))
         return {k_: float(np.mean(v_)) for k_, v_ in vals.items() if v_}
@@ -171,7 +171,7 @@ def traffic_summary(fetch_csv, write_csv, out_path, cmds):
     fetch_b, write_b = fe["attn"] * f_fac * 1024, wr["attn"] * w_fac * 1024
     pc = W.C4
     lines = [
-        "# HBM traffic of the prefill kernel fwd_bf16_kernel<D=64,HPW=4,causal> on the LFM2",
+        "# HBM traffic of the prefill kernel fwd16_kernel<bf16,D=64,HPW=4,causal> on the LFM2",
         "# prefill workload (B4 Hq32 Hkv8 S4096 D64 bf16, Q/K pre-rotated), per launch.",
         "# Counters are KiB per dispatch; each is scaled by expected/measured for a plain",
         f"# elementwise copy of {COPY_BYTES} bytes (read {COPY_BYTES}, write {COPY_BYTES}).",
@@ -373,7 +373,7 @@ def main():
                    "frac_of_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),
                    "kv_bytes": kv_bytes,
                    "ms_by_splits": {str(k_): round(v_, 4) for k_, v_ in split_ms.items()}},
-        "roofline": {"kernel": "fwd_bf16_kernel<D=64,HPW=4,causal>", "bound": "mfma",
+        "roofline": {"kernel": "fwd16_kernel<bf16,D=64,HPW=4,causal>", "bound": "mfma",
                      "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
                      "launch_ms": round(kern_ms, 4), "traffic": traffic},

@@ -24,7 +24,7 @@ import torch  # loads the HIP runtime that libattn.so then binds to
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
 
-ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_EMPTY_KV = 0, -1, -2, -3, -4
 EXPORTS = ("attn_fwd", "attn_fwd_masked", "attn_bwd_workspace_bytes", "attn_bwd", "attn_decode_workspace_bytes",
            "attn_decode_splitkv", "attn_prefill_kvcache", "rope_apply", "attn_last_error")
@@ -85,9 +85,11 @@ def _check(code):
 def _dtype_code(t):
     if t.dtype == torch.bfloat16:
         return ATTN_BF16
+    if t.dtype == torch.float16:
+        return ATTN_F16
     if t.dtype == torch.float32:
         return ATTN_F32
-    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16, float16 or float32)")
 
 
 def _ptr(t):
@@ -109,7 +111,7 @@ def _need_gpu(*ts):
 
 def attn_fwd(q, k, v, causal=False, scale=None, rope_base=0.0, o=None, lse=None, stream=None,
              want_lse=True):
-    """O, LSE = exact attention.  q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (bf16 or fp32).
+    """O, LSE = exact attention.  q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (bf16, fp16 or fp32).
 
     Returns (o [B,Sq,Hq,D] in q's dtype, lse [B,Hq,Sq] fp32 or None)."""
     _need_gpu(q, k, v, o, lse)

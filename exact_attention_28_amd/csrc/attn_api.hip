@@ -100,7 +100,7 @@ int fwd_padded(const void* q, const void* k, const void* v, void* o, float* lse,
                int Hkv, int Sq, int Skv, int D, int causal, float scale, float rope_base,
                int dtype, xattn::MaskView mask, hipStream_t stream) {
   const int Dp = D <= 64 ? 64 : 128;
-  const size_t es = dtype == ATTN_BF16 ? 2 : 4;
+  const size_t es = dtype == ATTN_F32 ? 4 : 2;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t qb = up((size_t)B * Sq * Hq * Dp * es), kb = up((size_t)B * Skv * Hkv * Dp * es);
   std::lock_guard<std::mutex> lock(g_mu);
@@ -123,16 +123,16 @@ int fwd_padded(const void* q, const void* k, const void* v, void* o, float* lse,
                                  (double)rope_base, stream);
     if (e != hipSuccess) return hip_status(e, "attn_fwd: rope table launch");
   }
-  const int dt = dtype == ATTN_BF16 ? 1 : 0;
+  const int dt = dtype;  // kernel format codes: 0 fp32, 1 bf16, 2 fp16
   if ((e = xattn::launch_pack_heads(q, qp, B, Sq, Hq, D, Dp, tab, Skv - Sq, dt, stream)) !=
           hipSuccess ||
       (e = xattn::launch_pack_heads(k, kp, B, Skv, Hkv, D, Dp, tab, 0, dt, stream)) != hipSuccess ||
       (e = xattn::launch_pack_heads(v, vp, B, Skv, Hkv, D, Dp, nullptr, 0, dt, stream)) !=
           hipSuccess)
     return hip_status(e, "attn_fwd: head-dim padding launch");
-  if (dtype == ATTN_BF16)
-    e = xattn::launch_fwd_bf16(qp, kp, vp, op, lse, B, Hq, Hkv, Sq, Skv, Dp, causal, scale,
-                               nullptr, stream, nullptr, 0, mask);
+  if (dtype != ATTN_F32)
+    e = xattn::launch_fwd16(qp, kp, vp, op, lse, B, Hq, Hkv, Sq, Skv, Dp, causal, scale, nullptr,
+                            dt, stream, nullptr, 0, mask);
   else
     e = xattn::launch_fwd_f32(qp, kp, vp, op, lse, B, Hq, Hkv, Sq, Skv, Dp, causal, scale,
                               nullptr, stream, mask);
@@ -159,7 +159,7 @@ int fwd(const char* fn, const void* q, const void* k, const void* v, void* o, fl
     return fail(ATTN_ERR_INVALID, "%s: rope_base must be finite", fn);
   const bool rope = rope_base > 0.f;
   if (rope && D % 2 != 0) return fail(ATTN_ERR_INVALID, "%s: RoPE needs an even head dim", fn);
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16)
     return fail(ATTN_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
   if (D > 128) return fail(ATTN_ERR_UNSUPPORTED, "%s: D=%d (built: up to 128)", fn, D);
   if (rope && Sq > Skv)
@@ -185,18 +185,18 @@ int fwd(const char* fn, const void* q, const void* k, const void* v, void* o, fl
     hipError_t e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), 0, Skv, D,
                                             (double)rope_base, stream);
     if (e != hipSuccess) return hip_status(e, "attn_fwd: rope table launch");
-    if (dtype == ATTN_BF16) {
+    if (dtype != ATTN_F32) {
       const size_t kb = (size_t)B * Skv * Hkv * D * 2;
       if ((st = grow(&db->kstage, &db->kstage_bytes, kb, "rotated K")) != ATTN_OK) return st;
-      e = xattn::launch_rope_rotate(k, db->kstage, B, Skv, Hkv, D, tab, 1, stream);
+      e = xattn::launch_rope_rotate(k, db->kstage, B, Skv, Hkv, D, tab, dtype, stream);
       if (e != hipSuccess) return hip_status(e, "attn_fwd: K rotation launch");
       kin = db->kstage;
     }
   }
   hipError_t e;
-  if (dtype == ATTN_BF16)
-    e = xattn::launch_fwd_bf16(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab,
-                               stream, nullptr, 0, mask);
+  if (dtype != ATTN_F32)
+    e = xattn::launch_fwd16(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab, dtype,
+                            stream, nullptr, 0, mask);
   else
     e = xattn::launch_fwd_f32(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab,
                               stream, mask);
@@ -257,7 +257,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     return fail(ATTN_ERR_INVALID, "attn_bwd: rope_base must be finite");
   const bool rope = rope_base > 0.f;
   if (rope && D % 2 != 0) return fail(ATTN_ERR_INVALID, "attn_bwd: RoPE needs an even head dim");
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16)
     return fail(ATTN_ERR_INVALID, "attn_bwd: unknown dtype %d", dtype);
   if (dtype != ATTN_BF16 || D != 64)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: built for bf16 with D=64 (dtype=%d D=%d)", dtype,
@@ -390,8 +390,8 @@ int attn_prefill_kvcache(const void* q, const void* k_new, const void* v_new, vo
   hipError_t e = xattn::launch_cache_append(k_new, v_new, kcache, vcache, cache_lens, B, Sq, Hkv,
                                             D, max_seqlen, tab, stream);
   if (e != hipSuccess) return hip_status(e, "attn_prefill_kvcache: append launch");
-  e = xattn::launch_fwd_bf16(q, kcache, vcache, o, lse, B, Hq, Hkv, Sq, max_seqlen, D, causal,
-                             scale, tab, stream, cache_lens, max_seqlen);
+  e = xattn::launch_fwd16(q, kcache, vcache, o, lse, B, Hq, Hkv, Sq, max_seqlen, D, causal, scale,
+                          tab, ATTN_BF16, stream, cache_lens, max_seqlen);
   return hip_status(e, "attn_prefill_kvcache: kernel launch");
 }
 
@@ -404,7 +404,7 @@ int rope_apply(void* x, int B, int S, int H, int D, int pos_offset, float rope_b
   if ((long long)pos_offset + S > 0x7fffffffLL)
     return fail(ATTN_ERR_INVALID, "rope_apply: positions overflow");
   if (!finite_pos(rope_base)) return fail(ATTN_ERR_INVALID, "rope_apply: rope_base must be finite and > 0");
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16)
     return fail(ATTN_ERR_INVALID, "rope_apply: unknown dtype %d", dtype);
   if (D > 256) return fail(ATTN_ERR_UNSUPPORTED, "rope_apply: D=%d (built: up to 256)", D);
 

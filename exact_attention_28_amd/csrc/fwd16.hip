@@ -1,4 +1,6 @@
-// fwd_bf16.hip — bf16 exact attention forward on gfx950 matrix cores.
+// fwd16.hip — exact attention forward on gfx950 matrix cores for 16-bit
+// inputs (bf16, or IEEE binary16 / fp16: the same kernel with the fp16 MFMA
+// and conversions; fp32 accumulation either way).
 //
 // What is computed is the tiled forward with online softmax of scirs2-neural
 // 0.4.3 (src/layers/flash_attention.rs): fn flash_attention_forward (query
@@ -17,23 +19,24 @@
 //    one kv head x (128 / HPW) positions, so every K/V tile fetched from HBM is
 //    reused by the whole head group.  Wave w owns columns [32w, 32w + 32).
 //  * Scores are produced transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand, the wave's
+//    v_mfma_f32_32x32x16_bf16 (_f16): K (from LDS) is the A operand, the wave's
 //    query fragment (kept in registers for the whole loop) the B operand.
 //    In the 32x32 accumulator a lane holds one query column and 16 key rows,
 //    so the row max / row sum are 15 in-lane ops plus one exchange with the
 //    lane 32 away, and the probabilities are already laid out as the B
 //    operand of the second contraction O^T += V^T P^T (no LDS round trip).
-//  * K tiles are stored row-major in LDS, V tiles transposed (d-major) so the
-//    A operand of O^T += V^T P^T is two 8-byte LDS reads per lane.  Both are
-//    double buffered: the next tile is loaded from HBM into registers with
-//    16-byte loads while the current one is consumed, then written to the
-//    other buffer; one barrier per tile.
+//  * K and V tiles are stored row-major in LDS (16-byte chunks XOR-swizzled
+//    per row) by direct HBM->LDS buffer loads, double buffered: the next
+//    tile's loads are in flight while the current one is consumed, with one
+//    barrier per tile.  The A operand of O^T += V^T P^T comes from the V tile
+//    by LDS transpose reads (ds_read_b64_tr_b16), two per lane per 16 keys.
 //  * Softmax runs in the base-2 domain: scale * log2(e) is applied by one FMA
 //    per score together with the max subtraction, exp2 is v_exp_f32.
 //  * RoPE on queries is applied while the query fragment is loaded (fp64
-//    rotation from the fp64 table, one rounding to bf16).  Keys are rotated
-//    once per call by the RoPE kernel before this one (each K tile is read by
-//    every query tile, so rotating it here would repeat the work Sq/128 times).
+//    rotation from the fp64 table, one rounding to the input format).  Keys
+//    are rotated once per call by the RoPE kernel before this one (each K tile
+//    is read by every query tile, so rotating it here would repeat the work
+//    Sq/128 times).
 //  * An additive mask (MASK) is read per lane as 16-byte chunks of 4 keys
 //    (the accumulator rows a lane holds come in runs of 4), issued at the top
 //    of each tile before the next tile's direct loads so that waiting for it
@@ -79,8 +82,8 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buf
   }
 }
 
-template <int D, int HPW, bool CAUSAL, bool ROPE, int NQB, bool MASK>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(
+template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB, bool MASK>
+__global__ __launch_bounds__(256) void fwd16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Skv_all,
     const int* __restrict__ kv_lens, int kv_rows, float scale_log2,
@@ -91,8 +94,10 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   constexpr int NDB = D / 32;                // 32-row blocks of O^T
   constexpr int NKS = D / 16;                // k-steps of the QK^T contraction
   static_assert(LD >= 1, "tile loads");
+  typedef Fmt16<T> F;
+  typedef typename F::v8 v8;
 
-  // K and V tiles live in LDS unpadded (row = D bf16), written by direct
+  // K and V tiles live in LDS unpadded (row = D 16-bit values), written by direct
   // HBM->LDS loads; 16-byte chunks are XOR-swizzled per row so the fragment
   // reads hit distinct banks (see kswz / vswz).
   // two buffers as separate arrays: with the loop unrolled by two, every LDS
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   }
 
   // ---- query fragments: lane holds q[pos, hh, 16ks + 8g .. +7] for every ks
-  bf16x8 qf[NQB][NKS];
+  v8 qf[NQB][NKS];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const u16* qp =
@@ -147,11 +152,11 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           double r0, r1;
-          rotate_pair((double)bf16_lo(wv[e]), (double)bf16_hi(wv[e]), tp[e], r0, r1);
-          wv[e] = f64_to_bf16_bits(r0) | (f64_to_bf16_bits(r1) << 16);
+          rotate_pair((double)F::lo(wv[e]), (double)F::hi(wv[e]), tp[e], r0, r1);
+          wv[e] = F::from_f64(r0) | (F::from_f64(r1) << 16);
         }
       }
-      qf[qb][ks] = __builtin_bit_cast(bf16x8, wv);
+      qf[qb][ks] = __builtin_bit_cast(v8, wv);
     }
   }
 
@@ -286,10 +291,9 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kc_[ka_off[blk][ks]]);
+        const v8 ka = *reinterpret_cast<const v8*>(&kc_[ka_off[blk][ks]]);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-          s[qb][blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], s[qb][blk], 0, 0, 0);
+        for (int qb = 0; qb < NQB; ++qb) s[qb][blk] = F::mfma(ka, qf[qb][ks], s[qb][blk]);
       }
     }
 
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     }
 
     // online softmax for this lane's query columns
-    bf16x8 pf[NQB][4];
+    v8 pf[NQB][4];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
@@ -355,11 +359,11 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
           ls += p;
         }
       l_run[qb] += ls;  // per half-wave partial; the halves are added after the loop
-      // probabilities as bf16 B operands: chunk kc covers keys 16kc .. 16kc+15
+      // probabilities as 16-bit B operands: chunk kc covers keys 16kc .. 16kc+15
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[qb][kc][e] = (__bf16)s[qb][kc >> 1][(kc & 1) * 8 + e];
+        for (int e = 0; e < 8; ++e) pf[qb][kc][e] = (T)s[qb][kc >> 1][(kc & 1) * 8 + e];
     }
 
     // O^T (D x 32) += V^T (D x 64) P^T (64 x 32); V^T fragments by transpose reads
@@ -371,10 +375,9 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
         const s16x4 hi = lds_read_tr16(&vc_[va_off[db][kc][1]]);
         const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
         const u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
-        const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
+        const v8 va = __builtin_bit_cast(v8, vv);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][kc], oacc[qb][db], 0, 0, 0);
+        for (int qb = 0; qb < NQB; ++qb) oacc[qb][db] = F::mfma(va, pf[qb][kc], oacc[qb][db]);
       }
     }
 
@@ -401,8 +404,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
         for (int a = 0; a < 4; ++a) {
           const int d = db * 32 + 8 * a + 4 * g;
           u32x2 pk;
-          pk[0] = pack_bf16(oacc[qb][db][4 * a] * inv, oacc[qb][db][4 * a + 1] * inv);
-          pk[1] = pack_bf16(oacc[qb][db][4 * a + 2] * inv, oacc[qb][db][4 * a + 3] * inv);
+          pk[0] = F::pack(oacc[qb][db][4 * a] * inv, oacc[qb][db][4 * a + 1] * inv);
+          pk[1] = F::pack(oacc[qb][db][4 * a + 2] * inv, oacc[qb][db][4 * a + 3] * inv);
           *reinterpret_cast<u32x2*>(op + d) = pk;
         }
       if (LSE != nullptr && g == 0)
@@ -412,8 +415,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   }
 }
 
-template <int D, int HPW, bool CAUSAL, bool ROPE, int NQB, bool MASK>
-static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB, bool MASK>
+static hipError_t go16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int Hq, int Hkv, int Sq, int Skv, const int* kv_lens, int kv_rows,
                           float scale, const double2* tab, MaskView mask, hipStream_t stream) {
   constexpr int NP = 128 * NQB / HPW;
@@ -421,7 +424,7 @@ static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, 
   const int n_bh = B * (Hq / HPW);
   const long long nblocks = (long long)n_qt * n_bh;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  fwd_bf16_kernel<D, HPW, CAUSAL, ROPE, NQB, MASK>
+  fwd16_kernel<T, D, HPW, CAUSAL, ROPE, NQB, MASK>
       <<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
           static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v),
           static_cast<u16*>(o), lse, Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale * kLog2e, tab,
@@ -433,61 +436,75 @@ static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, 
 // registers allow it); one block keeps small problems spread over more
 // workgroups (at least two per CU).  Masked runs use one block (the mask
 // values take the registers a second block would need).
-template <int D, int HPW, bool CAUSAL, bool ROPE>
-static hipError_t go_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+template <typename T, int D, int HPW, bool CAUSAL, bool ROPE>
+static hipError_t go16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int Hq, int Hkv, int Sq, int Skv, const int* kv_lens, int kv_rows,
                           float scale, const double2* tab, MaskView mask, hipStream_t stream) {
   if (mask.p != nullptr)
-    return go_bf16<D, HPW, CAUSAL, ROPE, 1, true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
+    return go16<T, D, HPW, CAUSAL, ROPE, 1, true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
                                                   kv_rows, scale, tab, mask, stream);
   if constexpr (D == 64) {
     const long long wg2 = (long long)((Sq + 256 / HPW - 1) / (256 / HPW)) * B * (Hq / HPW);
     if (wg2 >= 2 * 256)
-      return go_bf16<D, HPW, CAUSAL, ROPE, 2, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv,
+      return go16<T, D, HPW, CAUSAL, ROPE, 2, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv,
                                                      kv_lens, kv_rows, scale, tab, mask, stream);
   }
-  return go_bf16<D, HPW, CAUSAL, ROPE, 1, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
+  return go16<T, D, HPW, CAUSAL, ROPE, 1, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
                                                  kv_rows, scale, tab, mask, stream);
 }
 
-template <int D, bool CAUSAL, bool ROPE>
+template <typename T, int D, bool CAUSAL, bool ROPE>
 static hipError_t pick_hpw(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Sq, int Skv, const int* kv_lens,
                            int kv_rows, float scale, const double2* tab, MaskView mask,
                            hipStream_t stream) {
   const int G = Hq / Hkv;
   if (G % 8 == 0)
-    return go_bf16<D, 8, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
+    return go16<T, D, 8, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
                                        scale, tab, mask, stream);
   if (G % 4 == 0)
-    return go_bf16<D, 4, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
+    return go16<T, D, 4, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
                                        scale, tab, mask, stream);
   if (G % 2 == 0)
-    return go_bf16<D, 2, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
+    return go16<T, D, 2, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
                                        scale, tab, mask, stream);
-  return go_bf16<D, 1, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
+  return go16<T, D, 1, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
                                      scale, tab, mask, stream);
 }
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
-                           float scale, const double2* rope_tab, hipStream_t stream,
-                           const int* kv_lens, int kv_rows, MaskView mask) {
+template <typename T>
+static hipError_t launch_fmt(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                             float scale, const double2* rope_tab, hipStream_t stream,
+                             const int* kv_lens, int kv_rows, MaskView mask) {
   const bool rope = rope_tab != nullptr;
+#define XATTN_FWD16_CASE(DD, C, R)                                                         \
+  if (D == DD && (causal != 0) == C && rope == R)                                          \
+    return pick_hpw<T, DD, C, R>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale, \
+                                 rope_tab, mask, stream);
+  XATTN_FWD16_CASE(64, false, false)
+  XATTN_FWD16_CASE(64, true, false)
+  XATTN_FWD16_CASE(64, false, true)
+  XATTN_FWD16_CASE(64, true, true)
+  XATTN_FWD16_CASE(128, false, false)
+  XATTN_FWD16_CASE(128, true, false)
+  XATTN_FWD16_CASE(128, false, true)
+  XATTN_FWD16_CASE(128, true, true)
+#undef XATTN_FWD16_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                        const double2* rope_tab, int dtype, hipStream_t stream,
+                        const int* kv_lens, int kv_rows, MaskView mask) {
   if (kv_lens == nullptr) kv_rows = Skv;
-#define XATTN_BF16_CASE(DD, C, R)                                                          \
-  if (D == DD && (causal != 0) == C && rope == R)                                        \
-    return pick_hpw<DD, C, R>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale, \
-                              rope_tab, mask, stream);
-  XATTN_BF16_CASE(64, false, false)
-  XATTN_BF16_CASE(64, true, false)
-  XATTN_BF16_CASE(64, false, true)
-  XATTN_BF16_CASE(64, true, true)
-  XATTN_BF16_CASE(128, false, false)
-  XATTN_BF16_CASE(128, true, false)
-  XATTN_BF16_CASE(128, false, true)
-  XATTN_BF16_CASE(128, true, true)
-#undef XATTN_BF16_CASE
+  if (dtype == 1)
+    return launch_fmt<__bf16>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, rope_tab,
+                              stream, kv_lens, kv_rows, mask);
+  if (dtype == 2)
+    return launch_fmt<_Float16>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, rope_tab,
+                                stream, kv_lens, kv_rows, mask);
   return hipErrorInvalidValue;
 }
 

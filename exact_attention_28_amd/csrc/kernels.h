@@ -18,17 +18,17 @@ struct MaskView {
 
 // Prefill: q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D], o like q, lse [B,Hq,Sq] (nullable).
 // rope_tab: table rows for positions [0, Skv); query row i uses row Skv-Sq+i.
-// bf16 rotates only the queries in the kernel (keys arrive rotated); fp32
-// rotates queries and keys.  Null disables rotation.
-// bf16 with kv_lens non-null: k/v are caches of kv_rows rows per batch and
+// The 16-bit kernels (dtype 1 bf16, 2 fp16) rotate only the queries (keys
+// arrive rotated); fp32 rotates queries and keys.  Null disables rotation.
+// 16-bit with kv_lens non-null: k/v are caches of kv_rows rows per batch and
 // batch b attends to its first min(kv_lens[b], kv_rows - Sq) + Sq rows (Skv
 // is then unused; the table must cover kv_rows positions).  mask.p non-null
-// adds the mask to the scores (bf16 and fp32).
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
-                           float scale, const double2* rope_tab, hipStream_t stream,
-                           const int* kv_lens = nullptr, int kv_rows = 0,
-                           MaskView mask = MaskView());
+// adds the mask to the scores (all formats).
+hipError_t launch_fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                        const double2* rope_tab, int dtype, hipStream_t stream,
+                        const int* kv_lens = nullptr, int kv_rows = 0,
+                        MaskView mask = MaskView());
 
 // Cache append: rows t < Sq of k_new/v_new [B,Sq,Hkv,D] (bf16) go to rows
 // L_b + t of kcache/vcache [B,rows,Hkv,D] with L_b = min(max(lens[b], 0),
@@ -46,8 +46,8 @@ hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, 
 // t < npos, i < D/2, in fp64.
 hipError_t launch_rope_table(double2* tab, int pos0, int npos, int D, double base,
                              hipStream_t stream);
-// Rotate x [B,S,H,D] (dtype 0 fp32 / 1 bf16) into y (y may equal x); token t
-// uses table row t.
+// Rotate x [B,S,H,D] (dtype 0 fp32 / 1 bf16 / 2 fp16) into y (y may equal x);
+// token t uses table row t.
 hipError_t launch_rope_rotate(const void* x, void* y, int B, int S, int H, int D,
                               const double2* tab, int dtype, hipStream_t stream);
 
@@ -63,7 +63,7 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            hipStream_t stream);
 
 // Head dims other than 64/128: copy x [B,S,H,D] into y [B,S,H,Dp] with zero
-// columns past D (dtype 0 fp32 / 1 bf16), rotating pair i < D/2 of token t by
+// columns past D (dtype 0 fp32 / 1 bf16 / 2 fp16), rotating pair i < D/2 of token t by
 // table row pos0 + t when tab is non-null; and back: o [rows, D] from the first
 // D columns of op [rows, Dp].
 hipError_t launch_pack_heads(const void* x, void* y, int B, int S, int H, int D, int Dp,

@@ -15,8 +15,9 @@ namespace xattn {
 
 // y [rows, Dp] from x [rows, D] (rows = (b, t, h) of a [B, S, H, D] tensor):
 // columns >= D are zero; with tab, pair i < D/2 of token t is rotated by table
-// row pos0 + t (fp64, rounded once to the element type).
-template <bool BF16>
+// row pos0 + t (fp64, rounded once to the element type T: __bf16, _Float16 or
+// float).
+template <typename T>
 __global__ __launch_bounds__(256) void pack_heads_kernel(const void* __restrict__ xv,
                                                          void* __restrict__ yv, long long n, int S,
                                                          int H, int D, int Dp,
@@ -29,8 +30,10 @@ __global__ __launch_bounds__(256) void pack_heads_kernel(const void* __restrict_
     double val = 0.0;
     auto ld = [&](int c) -> double {
       const long long i = row * D + c;
-      if (BF16) return (double)bf16_lo(static_cast<const u16*>(xv)[i]);
-      return (double)static_cast<const float*>(xv)[i];
+      if constexpr (sizeof(T) == 2)
+        return (double)Fmt16<T>::lo(static_cast<const u16*>(xv)[i]);
+      else
+        return (double)static_cast<const float*>(xv)[i];
     };
     if (d < D) {
       if (tab != nullptr) {
@@ -43,8 +46,8 @@ __global__ __launch_bounds__(256) void pack_heads_kernel(const void* __restrict_
         val = ld(d);
       }
     }
-    if (BF16)
-      static_cast<u16*>(yv)[e] = (u16)f64_to_bf16_bits(val);
+    if constexpr (sizeof(T) == 2)
+      static_cast<u16*>(yv)[e] = (u16)Fmt16<T>::from_f64(val);
     else
       static_cast<float*>(yv)[e] = (float)val;
   }
@@ -71,16 +74,18 @@ hipError_t launch_pack_heads(const void* x, void* y, int B, int S, int H, int D,
                              const double2* tab, int pos0, int dtype, hipStream_t stream) {
   const long long n = (long long)B * S * H * Dp;
   if (dtype == 1)
-    pack_heads_kernel<true><<<grid_for(n), 256, 0, stream>>>(x, y, n, S, H, D, Dp, tab, pos0);
+    pack_heads_kernel<__bf16><<<grid_for(n), 256, 0, stream>>>(x, y, n, S, H, D, Dp, tab, pos0);
+  else if (dtype == 2)
+    pack_heads_kernel<_Float16><<<grid_for(n), 256, 0, stream>>>(x, y, n, S, H, D, Dp, tab, pos0);
   else
-    pack_heads_kernel<false><<<grid_for(n), 256, 0, stream>>>(x, y, n, S, H, D, Dp, tab, pos0);
+    pack_heads_kernel<float><<<grid_for(n), 256, 0, stream>>>(x, y, n, S, H, D, Dp, tab, pos0);
   return hipGetLastError();
 }
 
 hipError_t launch_unpack_heads(const void* op, void* o, long long rows, int D, int Dp, int dtype,
                                hipStream_t stream) {
   const long long n = rows * D;
-  if (dtype == 1)
+  if (dtype == 1 || dtype == 2)
     unpack_heads_kernel<u16><<<grid_for(n), 256, 0, stream>>>(static_cast<const u16*>(op),
                                                               static_cast<u16*>(o), n, D, Dp);
   else

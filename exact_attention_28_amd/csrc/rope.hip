@@ -38,8 +38,10 @@ hipError_t launch_rope_table(double2* tab, int pos0, int npos, int D, double bas
   return hipGetLastError();
 }
 
-// bf16, 4 pairs (16 bytes) per thread; needs D % 8 == 0.
-__global__ void rope_rotate_bf16x8(const u16* x, u16* y,
+// 16-bit formats (T = __bf16 or _Float16), 4 pairs (16 bytes) per thread;
+// needs D % 8 == 0.
+template <typename T>
+__global__ void rope_rotate_16x8(const u16* x, u16* y,
                                    long long nchunks, int S, int H, int D,
                                    const double2* __restrict__ tab) {
   const int cpr = D / 8;  // 16-byte chunks per head row
@@ -55,16 +57,17 @@ __global__ void rope_rotate_bf16x8(const u16* x, u16* y,
     for (int e = 0; e < 4; ++e) {
       const double2 cs = tab[(long long)t * half + part * 4 + e];
       double r0, r1;
-      rotate_pair((double)bf16_lo(w[e]), (double)bf16_hi(w[e]), cs, r0, r1);
-      r[e] = f64_to_bf16_bits(r0) | (f64_to_bf16_bits(r1) << 16);
+      rotate_pair((double)Fmt16<T>::lo(w[e]), (double)Fmt16<T>::hi(w[e]), cs, r0, r1);
+      r[e] = Fmt16<T>::from_f64(r0) | (Fmt16<T>::from_f64(r1) << 16);
     }
     *reinterpret_cast<u32x4*>(y + c * 8) = r;
   }
 }
 
-// Any even D: one pair per thread, bf16 (a uint32 holds the pair) or fp32.
-// x and y may alias (in-place rotation): each thread reads, then writes, only its own pair.
-template <bool BF16>
+// Any even D: one pair per thread, a 16-bit format (T = __bf16 or _Float16: a
+// uint32 holds the pair) or fp32 (T = float).  x and y may alias (in-place
+// rotation): each thread reads, then writes, only its own pair.
+template <typename T>
 __global__ void rope_rotate_pair(const void* xv, void* yv,
                                  long long npairs, int S, int H, int D,
                                  const double2* __restrict__ tab) {
@@ -76,10 +79,11 @@ __global__ void rope_rotate_pair(const void* xv, void* yv,
     const int t = (int)((row / H) % S);
     const double2 cs = tab[(long long)t * half + i];
     double r0, r1;
-    if (BF16) {
+    if constexpr (sizeof(T) == 2) {
       const uint32_t w = reinterpret_cast<const uint32_t*>(xv)[pidx];
-      rotate_pair((double)bf16_lo(w), (double)bf16_hi(w), cs, r0, r1);
-      reinterpret_cast<uint32_t*>(yv)[pidx] = f64_to_bf16_bits(r0) | (f64_to_bf16_bits(r1) << 16);
+      rotate_pair((double)Fmt16<T>::lo(w), (double)Fmt16<T>::hi(w), cs, r0, r1);
+      reinterpret_cast<uint32_t*>(yv)[pidx] =
+          Fmt16<T>::from_f64(r0) | (Fmt16<T>::from_f64(r1) << 16);
     } else {
       const float2 w = reinterpret_cast<const float2*>(xv)[pidx];
       rotate_pair((double)w.x, (double)w.y, cs, r0, r1);
@@ -93,21 +97,29 @@ hipError_t launch_rope_rotate(const void* x, void* y, int B, int S, int H, int D
   const long long rows = (long long)B * S * H;
   const int threads = 256;
   const long long max_blocks = 256LL * 8 * 4;  // a few resident waves per SIMD, grid-stride
-  if (dtype == 1 && D % 8 == 0) {
+  if (dtype != 0 && dtype != 1 && dtype != 2) return hipErrorInvalidValue;
+  if (dtype != 0 && D % 8 == 0) {
     const long long n = rows * (D / 8);
     long long blocks = (n + threads - 1) / threads;
     if (blocks > max_blocks) blocks = max_blocks;
-    rope_rotate_bf16x8<<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
-        static_cast<const u16*>(x), static_cast<u16*>(y), n, S, H, D, tab);
+    if (dtype == 1)
+      rope_rotate_16x8<__bf16><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
+          static_cast<const u16*>(x), static_cast<u16*>(y), n, S, H, D, tab);
+    else
+      rope_rotate_16x8<_Float16><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
+          static_cast<const u16*>(x), static_cast<u16*>(y), n, S, H, D, tab);
   } else {
     const long long n = rows * (D / 2);
     long long blocks = (n + threads - 1) / threads;
     if (blocks > max_blocks) blocks = max_blocks;
     if (dtype == 1)
-      rope_rotate_pair<true><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
+      rope_rotate_pair<__bf16><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
+          x, y, n, S, H, D, tab);
+    else if (dtype == 2)
+      rope_rotate_pair<_Float16><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
           x, y, n, S, H, D, tab);
     else
-      rope_rotate_pair<false><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
+      rope_rotate_pair<float><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
           x, y, n, S, H, D, tab);
   }
   return hipGetLastError();

@@ -41,6 +41,7 @@ extern "C" {
 typedef enum {
   ATTN_F32 = 0,  /* IEEE binary32 */
   ATTN_BF16 = 1, /* bfloat16 (8 significant bits) */
+  ATTN_F16 = 2,  /* IEEE binary16 (11 significant bits, subnormals kept) */
 } attn_dtype_t;
 
 typedef enum {
@@ -87,7 +88,9 @@ typedef enum {
  *   padded width's).  The padded copies live in a library-owned buffer.
  *   causal: 0 or 1;  scale: finite and > 0, used as given (the pages' default
  *   is 1/sqrt(D));  rope_base: > 0 enables RoPE (D even), <= 0 disables it
- *   dtype: ATTN_BF16 (bf16 MFMA, fp32 accumulation) or ATTN_F32 (fp32 throughout)
+ *   dtype: ATTN_BF16 or ATTN_F16 (16-bit MFMA of that format, fp32
+ *          accumulation; P enters the second product in the input format), or
+ *          ATTN_F32 (fp32 throughout)
  * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_EMPTY_KV (Skv == 0),
  *   ATTN_ERR_HIP.  With rope_base > 0 and bf16, the call may allocate the
  *   library's rotated-K staging buffer (B*Skv*Hkv*D*2 bytes) and RoPE table.

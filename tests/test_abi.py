@@ -56,7 +56,11 @@ def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=4, Hkv=2, Sq=8, 
     (dict(rope=float("nan")), xa.ATTN_ERR_INVALID),
     (dict(D=63, rope=10000.0), xa.ATTN_ERR_INVALID),
     (dict(dtype=7), xa.ATTN_ERR_INVALID),
+    (dict(dtype=3), xa.ATTN_ERR_INVALID),
+    (dict(dtype=-1), xa.ATTN_ERR_INVALID),
     (dict(D=129), xa.ATTN_ERR_UNSUPPORTED),
+    (dict(D=129, dtype=2), xa.ATTN_ERR_UNSUPPORTED),
+    (dict(D=63, rope=10000.0, dtype=2), xa.ATTN_ERR_INVALID),
     (dict(D=256), xa.ATTN_ERR_UNSUPPORTED),
     (dict(Sq=16, Skv=8, rope=10000.0), xa.ATTN_ERR_UNSUPPORTED),
 ])
@@ -160,6 +164,7 @@ def _bwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAK
     (dict(D=63, rope=100.0), xa.ATTN_ERR_INVALID),
     (dict(dtype=9), xa.ATTN_ERR_INVALID),
     (dict(dtype=0), xa.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=2), xa.ATTN_ERR_UNSUPPORTED),
     (dict(D=128), xa.ATTN_ERR_UNSUPPORTED),
     (dict(Sq=16, Skv=8, rope=10000.0), xa.ATTN_ERR_UNSUPPORTED),
 ])

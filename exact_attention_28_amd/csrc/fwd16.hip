@@ -37,11 +37,19 @@
 //    are rotated once per call by the RoPE kernel before this one (each K tile
 //    is read by every query tile, so rotating it here would repeat the work
 //    Sq/128 times).
-//  * An additive mask (MASK) is read per lane as 16-byte chunks of 4 keys
-//    (the accumulator rows a lane holds come in runs of 4), issued at the top
-//    of each tile before the next tile's direct loads so that waiting for it
-//    never waits for the prefetch; it enters the scores as
-//    fma(s, scale * log2(e), mask * log2(e)).
+//  * An additive mask enters the scores as fma(s, scale, mask), and the
+//    softmax then scales by log2(e) in its exp2 argument.  A lane needs, per
+//    tile, its query row's mask at its 32 keys, which come in runs of 4
+//    (accumulator rows 4a..4a+3).  MASK = 3 (D = 64, 16-byte aligned mask
+//    shared by all heads, two or more heads per workgroup): the workgroup's
+//    NP query rows x 64 keys go to LDS by direct loads that cover 4 rows of
+//    256 bytes per instruction (chunks XOR-swizzled per row), double
+//    buffered and issued with the K/V tile one tile ahead; every wave reads
+//    its runs of 4 without bank conflicts.  MASK = 2 (the same, per-head
+//    masks or one head per workgroup): each wave stages its own 32 rows in a
+//    single buffer, refilled in the middle of a tile once its reads are done.
+//    MASK = 1 (any other mask, D = 128): each lane loads its runs of 4
+//    itself, 8 loads per tile that each touch 32 rows.
 //  * Workgroups are issued heaviest-first under the causal mask, and the
 //    (batch, head group) index is the fastest-varying part of the block index
 //    so that the workgroups of one head group land on one XCD (block i runs on
@@ -82,12 +90,16 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buf
   }
 }
 
-template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB, bool MASK>
-__global__ __launch_bounds__(256) void fwd16_kernel(
+// The shared-mask variant with 4 or 8 heads per workgroup needs 40-48 KiB of
+// LDS, so three workgroups fit a CU if the registers allow three waves per
+// SIMD (<= 168 VGPRs, reached without spills; measured 6 % faster).
+template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB, int MASK>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(MASK == 3 && HPW >= 4 ? 3 : 1))) void fwd16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Skv_all,
     const int* __restrict__ kv_lens, int kv_rows, float scale_log2,
-    const double2* __restrict__ tab, int n_qt, int n_bh, MaskView mask) {
+    const double2* __restrict__ tab, int n_qt, int n_bh, MaskView mask, float scale) {
   constexpr int BM = 128 * NQB, BN = 64, NP = BM / HPW;
   constexpr int KCH = D / 8;                 // 16-byte chunks per row
   constexpr int LD = BN * KCH / 256;         // 16-byte chunks per thread per tile (K and V each)
@@ -108,6 +120,11 @@ __global__ __launch_bounds__(256) void fwd16_kernel(
   __shared__ __attribute__((aligned(16))) u16 Vs0[BN * D];
   __shared__ __attribute__((aligned(16))) u16 Ks1[BN * D];
   __shared__ __attribute__((aligned(16))) u16 Vs1[BN * D];
+  // MASK = 2: per wave 32 query rows x 64 keys of fp32 mask (8 KiB);
+  // MASK = 3: the workgroup's NP rows x 64 keys, two buffers
+  __shared__ __attribute__((aligned(16))) float Ms[MASK == 2 ? 4 * 32 * BN : 1];
+  __shared__ __attribute__((aligned(16))) float Mx0[MASK == 3 ? NP * BN : 1];
+  __shared__ __attribute__((aligned(16))) float Mx1[MASK == 3 ? NP * BN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
@@ -161,14 +178,14 @@ __global__ __launch_bounds__(256) void fwd16_kernel(
   }
 
   // with a mask, the scores are scaled (and the mask added) right after the
-  // contraction, so the softmax below runs with unit scale
-  const float sl = MASK ? 1.f : scale_log2;
+  // contraction, so the softmax below only converts to base 2
+  const float sl = MASK ? kLog2e : scale_log2;
   const float* mrow[NQB];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb)
-    mrow[qb] = MASK ? mask.p + b * mask.bs + hh[qb] * mask.hs +
-                          (long long)(qvalid[qb] ? pos[qb] : 0) * mask.rs
-                    : nullptr;
+    mrow[qb] = MASK == 1 ? mask.p + b * mask.bs + hh[qb] * mask.hs +
+                               (long long)(qvalid[qb] ? pos[qb] : 0) * mask.rs
+                         : nullptr;
 
   int kv_end = Skv;
   if (CAUSAL) kv_end = min(Skv, min(p0 + NP, Sq) - 1 + off + 1);
@@ -194,6 +211,60 @@ __global__ __launch_bounds__(256) void fwd16_kernel(
     const int sl = (w * LD + i) * 64 + lane, row = sl / KCH, phys = sl % KCH;
     koff[i] = (uint32_t)row * row_bytes + (uint32_t)(phys ^ kswz<D>(row)) * 16u;
     voff[i] = (uint32_t)row * row_bytes + (uint32_t)(phys ^ vswz<D>(row)) * 16u;
+  }
+  // MASK = 2: this wave's mask rows r = 0..31 (its query columns) through a
+  // buffer resource based at the wave's first head; direct-load instruction i
+  // fills LDS rows 4i .. 4i+3, lane l the physical chunk l % 16 of row
+  // 4i + l / 16, which holds the row's logical chunk (l % 16) ^ (row % 16).
+  // The host takes this path only when every offset fits in 31 bits and Skv is
+  // a multiple of 4, so the resource's range ends on a chunk boundary: past the
+  // last valid element whole chunks read zeros.
+  // MASK = 3: rows r = 0..NP-1 are positions p0 + r; wave w issues
+  // instructions i < NI of the NP / 4 that fill them (LDS rows 4(w NI + i) ..
+  // +3), and lane (c, g) reads row (32 w + c) mod NP, its own position.
+  constexpr int NI = MASK == 3 ? NP / 16 : 8;
+  __amdgpu_buffer_rsrc_t rm;
+  uint32_t moff[NI];
+  int mrd[2][4];  // LDS float offset of this lane's run (blk, a)
+  float* Mw = Ms + w * 32 * BN;
+  if constexpr (MASK == 3) {
+    const long long last = (long long)(Sq - 1) * mask.rs + Skv;
+    const uint32_t mbytes = (uint32_t)min(last * 4, 0xFFFFFFFFLL);
+    rm = __builtin_amdgcn_make_buffer_rsrc((void*)(mask.p + b * mask.bs), (short)0, mbytes,
+                                           kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = 4 * (w * NI + i) + (lane >> 4);
+      int pr = p0 + r;
+      pr = pr < Sq ? pr : 0;
+      const int lc = (lane & 15) ^ (r & 15);
+      moff[i] = (uint32_t)(((long long)pr * mask.rs + 4 * lc) * 4);
+    }
+    const int r = (w * 32 + c) % NP;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) mrd[blk][a] = r * BN + (((8 * blk + 2 * a + g) ^ (r & 15)) << 2);
+  }
+  if constexpr (MASK == 2) {
+    const int hw = h0 + (w * 32) / NP;
+    const long long last = (long long)(Hq - 1 - hw) * mask.hs + (long long)(Sq - 1) * mask.rs + Skv;
+    const uint32_t mbytes = (uint32_t)min(last * 4, 0xFFFFFFFFLL);
+    rm = __builtin_amdgcn_make_buffer_rsrc((void*)(mask.p + b * mask.bs + hw * mask.hs), (short)0,
+                                           mbytes, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4), gc = w * 32 + r;
+      const int hr = h0 + gc / NP;
+      int pr = p0 + gc % NP;
+      pr = pr < Sq ? pr : 0;
+      const int lc = (lane & 15) ^ (r & 15);
+      moff[i] = (uint32_t)(((long long)(hr - hw) * mask.hs + (long long)pr * mask.rs + 4 * lc) * 4);
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) mrd[blk][a] = c * BN + (((8 * blk + 2 * a + g) ^ (c & 15)) << 2);
   }
   auto dma = [&](int k0, u16* kb, u16* vb) {
     dma_tile<LD>(rk, rv, kb + w * LD * 64 * 8, vb + w * LD * 64 * 8, koff, voff,
@@ -242,14 +313,20 @@ __global__ __launch_bounds__(256) void fwd16_kernel(
     l_run[qb] = 0.f;
   }
 
-  if (ntiles > 0) dma(0, Ks0, Vs0);
+  if (ntiles > 0) {
+    dma(0, Ks0, Vs0);
+    if constexpr (MASK == 2) dma_rows<8>(rm, reinterpret_cast<u16*>(Mw), moff, 0u);
+    if constexpr (MASK == 3) dma_rows<NI>(rm, reinterpret_cast<u16*>(Mx0 + w * NI * 256), moff, 0u);
+  }
   // everything the prologue loaded (query fragments, first tile) has landed
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // one key/value tile: its K and V are in (kc_, vc_); the next tile is loaded
   // into (kn_, vn_), last read in the previous step, which every wave has left
-  auto tile = [&](int t, const u16* kc_, const u16* vc_, u16* kn_, u16* vn_) {
+  // (likewise the shared mask rows, MASK = 3, in mc_ and mn_)
+  auto tile = [&](int t, const u16* kc_, const u16* vc_, u16* kn_, u16* vn_, const float* mc_,
+                  float* mn_) {
     const int k0 = t * BN;
     // mask values of this lane's 32 (query, key) pairs: keys
     // k0 + 32 blk + 8a + 4g + e at accumulator row 4a + e; 0 past Skv.
@@ -278,8 +355,12 @@ __global__ __launch_bounds__(256) void fwd16_kernel(
             }
           }
     };
-    if constexpr (MASK && D == 64) load_mask();
-    if (t + 1 < ntiles) dma(k0 + BN, kn_, vn_);
+    if constexpr (MASK == 1 && D == 64) load_mask();
+    if (t + 1 < ntiles) {
+      dma(k0 + BN, kn_, vn_);
+      if constexpr (MASK == 3)
+        dma_rows<NI>(rm, reinterpret_cast<u16*>(mn_ + w * NI * 256), moff, (uint32_t)(k0 + BN) * 4u);
+    }
 
     // S^T (64 keys x 32 queries per block) = K_tile Q^T
     f32x16 s[NQB][2];
@@ -297,15 +378,41 @@ __global__ __launch_bounds__(256) void fwd16_kernel(
       }
     }
 
-    if constexpr (MASK) {
-      if constexpr (D != 64) load_mask();
+    if constexpr (MASK == 3) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(mc_ + mrd[blk][a]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mv[0][blk][4 * a + e] = x[e];
+        }
+    }
+    if constexpr (MASK == 2) {
+      // this tile's rows landed with the previous end-of-tile wait
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(Mw + mrd[blk][a]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mv[0][blk][4 * a + e] = x[e];
+        }
+      // the reads are done before the next tile's rows overwrite the area
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < ntiles)
+        dma_rows<8>(rm, reinterpret_cast<u16*>(Mw), moff, (uint32_t)(k0 + BN) * 4u);
+    }
+    if constexpr (MASK != 0) {
+      if constexpr (MASK == 1 && D != 64) load_mask();
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            s[qb][blk][r] = fmaf(s[qb][blk][r], scale_log2, mv[qb][blk][r] * kLog2e);
+            s[qb][blk][r] = fmaf(s[qb][blk][r], scale, mv[qb][blk][r]);
     }
 
     // mask: key rows past Skv, and keys after the query under the causal rule
@@ -386,8 +493,8 @@ __global__ __launch_bounds__(256) void fwd16_kernel(
     __syncthreads();
   };
   for (int t = 0; t < ntiles; t += 2) {
-    tile(t, Ks0, Vs0, Ks1, Vs1);
-    if (t + 1 < ntiles) tile(t + 1, Ks1, Vs1, Ks0, Vs0);
+    tile(t, Ks0, Vs0, Ks1, Vs1, Mx0, Mx1);
+    if (t + 1 < ntiles) tile(t + 1, Ks1, Vs1, Ks0, Vs0, Mx1, Mx0);
   }
 
 #pragma unroll
@@ -415,7 +522,7 @@ __global__ __launch_bounds__(256) void fwd16_kernel(
   }
 }
 
-template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB, bool MASK>
+template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB, int MASK>
 static hipError_t go16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int Hq, int Hkv, int Sq, int Skv, const int* kv_lens, int kv_rows,
                           float scale, const double2* tab, MaskView mask, hipStream_t stream) {
@@ -428,7 +535,7 @@ static hipError_t go16(const void* q, const void* k, const void* v, void* o, flo
       <<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
           static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v),
           static_cast<u16*>(o), lse, Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale * kLog2e, tab,
-          n_qt, n_bh, mask);
+          n_qt, n_bh, mask, scale);
   return hipGetLastError();
 }
 
@@ -440,16 +547,34 @@ template <typename T, int D, int HPW, bool CAUSAL, bool ROPE>
 static hipError_t go16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int Hq, int Hkv, int Sq, int Skv, const int* kv_lens, int kv_rows,
                           float scale, const double2* tab, MaskView mask, hipStream_t stream) {
-  if (mask.p != nullptr)
-    return go16<T, D, HPW, CAUSAL, ROPE, 1, true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
-                                                  kv_rows, scale, tab, mask, stream);
+  if (mask.p != nullptr) {
+    // staged mask rows for D = 64 when the loads can be 16-byte, the end of
+    // the valid data (Skv keys into the last row) falls on a 16-byte boundary
+    // (a load that straddles the buffer's range end may read zeros as a whole),
+    // and every per-lane offset (a head step, a query row, a tile past the
+    // keys) fits in 31 bits
+    if constexpr (D == 64) {
+      const long long reach = (mask.hs + (long long)Sq * mask.rs + Skv + 2 * 64) * 4;
+      if (mask.vec && Skv % 4 == 0 && reach < (1LL << 31)) {
+        // rows shared by the workgroup's heads when the mask is the same for all
+        if constexpr (HPW >= 2)
+          if (mask.hs == 0)
+            return go16<T, D, HPW, CAUSAL, ROPE, 1, 3>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv,
+                                                       kv_lens, kv_rows, scale, tab, mask, stream);
+        return go16<T, D, HPW, CAUSAL, ROPE, 1, 2>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
+                                                   kv_rows, scale, tab, mask, stream);
+      }
+    }
+    return go16<T, D, HPW, CAUSAL, ROPE, 1, 1>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
+                                               kv_rows, scale, tab, mask, stream);
+  }
   if constexpr (D == 64) {
     const long long wg2 = (long long)((Sq + 256 / HPW - 1) / (256 / HPW)) * B * (Hq / HPW);
     if (wg2 >= 2 * 256)
-      return go16<T, D, HPW, CAUSAL, ROPE, 2, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv,
+      return go16<T, D, HPW, CAUSAL, ROPE, 2, 0>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv,
                                                      kv_lens, kv_rows, scale, tab, mask, stream);
   }
-  return go16<T, D, HPW, CAUSAL, ROPE, 1, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
+  return go16<T, D, HPW, CAUSAL, ROPE, 1, 0>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
                                                  kv_rows, scale, tab, mask, stream);
 }
 

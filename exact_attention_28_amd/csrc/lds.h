@@ -23,6 +23,8 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const u16* p) {
 
 // s_waitcnt with vmcnt(0) and the other counters unconstrained.
 constexpr int kWaitVmcnt0 = 0x0F70;
+// s_waitcnt with lgkmcnt(0) (LDS and scalar loads) and the others unconstrained.
+constexpr int kWaitLgkm0 = 0xC07F;
 
 __device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(u16* p) {
   return (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) char*)(p));

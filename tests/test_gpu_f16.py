@@ -83,10 +83,12 @@ def test_f16_variants(case):
     check_f16(_np(o), _np(lse), o_ref, lse_ref, f"f16 {case}")
 
 
-def test_f16_masked():
-    """fp16 with an additive mask: per (batch, head), -inf entries, RoPE."""
-    B, Hq, Hkv, Sq, Skv, D = 2, 8, 2, 150, 211, 64
-    say("case f16 masked")
+@pytest.mark.parametrize("Skv", [211, 212])
+def test_f16_masked(Skv):
+    """fp16 with an additive mask: per (batch, head), -inf entries, RoPE; 211
+    keys read the mask per lane, 212 stage it through LDS."""
+    B, Hq, Hkv, Sq, D = 2, 8, 2, 150, 64
+    say("case f16 masked", Skv)
     rng = np.random.default_rng(21)
     q, k, v = _inputs(rng, B, Hq, Hkv, Sq, Skv, D)
     m = (rng.standard_normal((B, Hq, Sq, Skv)) * 2.0).astype(np.float32)

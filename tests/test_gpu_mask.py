@@ -7,7 +7,10 @@ The bars are those of the unmasked forward (bf16: O max-abs 2e-2, rel-L2
 form the entry point takes (one [Sq, Skv] mask, per head, per batch and head,
 a per-key padding row), with row lengths that do and do not allow 16-byte
 loads, together with the causal flag, RoPE, grouped heads and padded head
-dims.  Rows whose keys are all hidden give O = 0 and lse = -inf.
+dims.  At D = 64, masks whose rows allow 16-byte loads and whose key count is
+a multiple of 4 are staged through LDS by the kernel (per wave, or once per
+workgroup when every head shares the mask); the others are read per lane: all
+three paths are covered, and one test checks that they give the same bits.  Rows whose keys are all hidden give O = 0 and lse = -inf.
 """
 import json
 import math
@@ -86,6 +89,9 @@ MASK_CASES = [  # B, Hq, Hkv, Sq, Skv, D, causal, rope, mask shape ('s' [Sq,Skv]
     (1, 3, 3, 64, 64, 64, True, 0.0, "bh"),        # one tile
     (2, 4, 1, 1, 517, 64, False, 0.0, "bh"),       # one query row
     (1, 4, 2, 50, 90, 40, True, 10000.0, "s"),     # padded head dim
+    (1, 16, 2, 96, 192, 64, False, 0.0, "h"),      # LDS-staged rows, a wave spans two heads
+    (2, 4, 2, 130, 256, 64, True, 10000.0, "bh"),  # LDS-staged rows, two heads per workgroup
+    (1, 16, 2, 100, 256, 64, True, 10000.0, "s"),  # rows shared by 8 heads of a workgroup
 ]
 
 
@@ -130,8 +136,8 @@ def test_masked_f32(case):
 def test_fully_hidden_rows_and_strided_mask():
     """Rows whose keys are all -inf give O = 0 and lse = -inf; a mask that is a
     strided view (rows of a wider array, a row pitch that rules out 16-byte
-    loads) and one broadcast by expand() give the same bits as their contiguous
-    copies."""
+    loads: read per lane) and one broadcast by expand() give the same bits as
+    their contiguous copies (staged through LDS)."""
     B, Hq, Hkv, Sq, Skv, D = 2, 4, 2, 70, 100, 64
     rng = np.random.default_rng(11)
     q = W.f32_to_bf16_bits(rng.standard_normal((B, Sq, Hq, D), dtype=np.float32))

@@ -147,6 +147,64 @@ def profile_kernel(reps):
     log("profile-kernel done")
 
 
+def profile_decode(reps):
+    """For counter runs: `reps` split-KV decode calls (split + merge, 16
+    splits) on the decode workload, then `reps` launches of the calibration
+    copy."""
+    dc = W.C5
+    dq_np, kc_np, vc_np, sl_np = W.decode_inputs(dc)
+    dq, kc, vc = W.to_device(dq_np), W.to_device(kc_np), W.to_device(vc_np)
+    sl = torch.from_numpy(sl_np).cuda()
+    do = torch.empty_like(dq)
+    ws = torch.empty(xa.attn_decode_workspace_bytes(dc.B, dc.Hq, dc.D, 16), dtype=torch.uint8,
+                     device="cuda")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        xa.attn_decode_splitkv(dq, kc, vc, sl, 16, scale=dc.scale, o=do, workspace=ws)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+    kv_bytes = int(sl_np.astype(np.int64).sum()) * dc.Hkv * dc.D * 2 * 2
+    log(f"profile-decode done (algorithmic KV bytes per call {kv_bytes})")
+
+
+def counters_summary(csv_path, match, out_path, title, cmds):
+    """Per-dispatch means of every counter in a rocprofv3 counter_collection
+    CSV for the kernels whose name contains `match`, with the calibration
+    copy's FETCH_SIZE / WRITE_SIZE when present."""
+    import csv
+    vals, copy = {}, {}
+    for path in csv_path.split(","):
+        for r in csv.DictReader(open(path)):
+            name, cn = r["Kernel_Name"], r["Counter_Name"]
+            if match in name:
+                vals.setdefault(cn, []).append(float(r["Counter_Value"]))
+            elif "elementwise" in name and "add" in name.lower():  # the copy, not the fill
+                copy.setdefault(cn, []).append(float(r["Counter_Value"]))
+    lines = [f"# {title}", "# Per-dispatch means over the matching dispatches "
+             f"(kernel name containing '{match}').", "# Commands (from the repository root, "
+             "TMPDIR=/tmp):", *[f"#   {c}" for c in cmds]]
+    if match.startswith("fwd16"):
+        lines.append(f"kernel_source_sha256_16: {kernel_hash()}")
+    for cn in sorted(vals):
+        lines.append(f"{cn}: {np.mean(vals[cn]):.6g}  (dispatches: {len(vals[cn])})")
+    for cn in sorted(copy):
+        lines.append(f"calibration_copy_{cn}: {np.mean(copy[cn]):.6g}  "
+                     f"(copy of {COPY_BYTES} bytes)")
+    # byte counters (KiB per dispatch) scaled by expected / measured for the copy
+    for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+        if cn in vals and copy.get(cn) and np.mean(copy[cn]) > 0:
+            fac = COPY_BYTES / 1024 / np.mean(copy[cn])
+            lines.append(f"{cn}_bytes_per_dispatch_scaled: {np.mean(vals[cn]) * fac * 1024:.0f}"
+                         f"  (scale {fac:.4f})")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_summary(fetch_csv, write_csv, out_path, cmds):
     """Writes the traffic summary read by read_traffic() from two rocprofv3
     counter_collection CSVs (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch).
@@ -207,9 +265,16 @@ def main():
                     help="write the traffic summary from two rocprofv3 counter CSVs")
     ap.add_argument("--traffic-cmd", action="append", default=[],
                     help="command line recorded in the traffic summary (repeatable)")
+    ap.add_argument("--profile-decode", type=int, default=0, metavar="REPS",
+                    help="only run the split-KV decode REPS times, then a calibration copy")
+    ap.add_argument("--counters-summary", nargs=4, metavar=("CSV", "MATCH", "OUT", "TITLE"),
+                    help="write per-dispatch counter means of kernels matching MATCH")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary, TRAFFIC_FILE, args.traffic_cmd)
+        return
+    if args.counters_summary:
+        counters_summary(*args.counters_summary, args.traffic_cmd)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
@@ -219,6 +284,9 @@ def main():
     torch.cuda.set_device(0)
     if args.profile_kernel:
         profile_kernel(args.profile_kernel)
+        return
+    if args.profile_decode:
+        profile_decode(args.profile_decode)
         return
     stream = torch.cuda.current_stream()
 

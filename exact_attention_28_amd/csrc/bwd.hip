@@ -275,26 +275,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                          vf[ks], dp[qb], 0, 0, 0);
       }
 
-    // P = exp2(c s - lse2), dS = P (dP - D); lane holds tile rows
+    // P = exp2(c s - lse2) in place of S; lane holds tile rows
     // 32 qb + 8 a + 4 g + e (a, e < 4) of column `key`
-    const bool need_mask = CAUSAL && (kw0 + 31 > p0 + off);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&ls[32 * qb + 8 * a + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[qb][4 * a + e] = __builtin_amdgcn_exp2f(fmaf(s[qb][4 * a + e], scale_log2, -l4[e]));
+      }
+    // causal: zero P above the diagonal on the tiles the diagonal crosses, in a
+    // wave-uniform branch (a mask test inside the loop above would become
+    // selects executed on every tile)
+    if (CAUSAL && kw0 + 31 > p0 + off) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key > p0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3) + off) s[qb][r] = 0.f;
+    }
+    // dS = P (dP - D); P and dS as bf16 B operands
     bf16x8 pf[4], sf[4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int row = 32 * qb + 8 * a + 4 * g;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&ls[row]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&ds[row]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&ds[32 * qb + 8 * a + 4 * g]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * a + e;
-          float pr = __builtin_amdgcn_exp2f(fmaf(s[qb][r], scale_log2, -l4[e]));
-          if (need_mask && key > p0 + row + e + off) pr = 0.f;
-          const float dsv = pr * (dp[qb][r] - d4[e]);
           // k slot r of query block qb: chunk 2 qb + r / 8, element r mod 8
-          pf[2 * qb + r / 8][r % 8] = (__bf16)pr;
-          sf[2 * qb + r / 8][r % 8] = (__bf16)dsv;
+          pf[2 * qb + r / 8][r % 8] = (__bf16)s[qb][r];
+          sf[2 * qb + r / 8][r % 8] = (__bf16)(s[qb][r] * (dp[qb][r] - d4[e]));
         }
       }
 
@@ -443,17 +457,28 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_frag(vs_, 32 * kb, c, g, ks),
                                                          of[ks], dp[kb], 0, 0, 0);
       }
-    // P^T, dS^T; lane holds keys k0 + 32 kb + 8 a + 4 g + e of its query
-    const bool need_mask = (k0 + BN > Skv) || (CAUSAL && k0 + BN - 1 > first_q);
+    // P^T in place of S^T; lane holds keys k0 + 32 kb + 8 a + 4 g + e of its
+    // query.  Keys at or past Skv need no mask here: their K rows read as
+    // zero, so their dS contributes nothing to dQ = K^T dS.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -l2));
+    // causal: zero P above the diagonal on the tiles the diagonal crosses (a
+    // wave-uniform branch)
+    if (CAUSAL && k0 + BN - 1 > first_q) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) > qlim) s[kb][r] = 0.f;
+    }
+    // dS^T = P^T (dP^T - D) as bf16 B operands
     bf16x8 sf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -l2));
-        if (need_mask && k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) > qlim) pr = 0.f;
-        sf[2 * kb + r / 8][r % 8] = (__bf16)(pr * (dp[kb][r] - dl));
-      }
+      for (int r = 0; r < 16; ++r) sf[2 * kb + r / 8][r % 8] = (__bf16)(s[kb][r] * (dp[kb][r] - dl));
     // dQ^T += K^T dS^T (rows d, columns queries)
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)

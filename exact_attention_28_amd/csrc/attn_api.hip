@@ -259,9 +259,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (rope && D % 2 != 0) return fail(ATTN_ERR_INVALID, "attn_bwd: RoPE needs an even head dim");
   if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16)
     return fail(ATTN_ERR_INVALID, "attn_bwd: unknown dtype %d", dtype);
-  if (dtype != ATTN_BF16 || D != 64)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: built for bf16 with D=64 (dtype=%d D=%d)", dtype,
-                D);
+  if (dtype == ATTN_F32 || D != 64)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: built for bf16 and fp16 with D=64 (dtype=%d D=%d)",
+                dtype, D);
   if (rope && Sq > Skv)
     return fail(ATTN_ERR_UNSUPPORTED,
                 "attn_bwd: RoPE with Sq > Skv would place queries at negative positions");
@@ -293,8 +293,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
       return st;
     ws = db->bwd_ws;
   }
-  hipError_t e = xattn::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D,
-                                        causal, scale, tab, ws, stream);
+  hipError_t e = xattn::launch_bwd16(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D,
+                                     causal, scale, tab, dtype, ws, stream);
   return hip_status(e, "attn_bwd: kernel launch");
 }
 

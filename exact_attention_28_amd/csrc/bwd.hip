@@ -1,4 +1,6 @@
-// bwd.hip — attention backward on gfx950 for bf16 inputs with D = 64.
+// bwd.hip — attention backward on gfx950 for 16-bit inputs (bf16, or IEEE
+// binary16 / fp16 through the same kernels with that format's MFMA and
+// conversions) with D = 64.
 //
 // The gradient of O = softmax(scale * Q~ K~^T) V for an upstream gradient dO,
 // as in the FA-2 backward per head of scirs2-neural 0.4.3
@@ -53,21 +55,25 @@ __device__ __forceinline__ int bswz(int row) {
   return ((x & 1) << 2) | (x >> 1);
 }
 
-// element offset of (row, logical column) in a swizzled 64-wide bf16 tile
+// element offset of (row, logical column) in a swizzled 64-wide 16-bit tile
 __device__ __forceinline__ int tile_off(int row, int col) {
   return row * kD + (((col >> 3) ^ bswz(row)) << 3) + (col & 7);
 }
 
 // MFMA A operand from a swizzled tile by rows: lane (r = lane mod 32, g)
 // receives row row0 + r, columns 16 ks + 8 g .. +7.
-__device__ __forceinline__ bf16x8 rows_frag(const u16* t, int row0, int c, int g, int ks) {
-  return *reinterpret_cast<const bf16x8*>(&t[tile_off(row0 + c, 16 * ks + 8 * g)]);
+template <typename T>
+__device__ __forceinline__ typename Fmt16<T>::v8 rows_frag(const u16* t, int row0, int c, int g,
+                                                           int ks) {
+  return *reinterpret_cast<const typename Fmt16<T>::v8*>(&t[tile_off(row0 + c, 16 * ks + 8 * g)]);
 }
 
 // MFMA A operand of the transposed tile (columns become rows): lane (i, g)
 // receives column 32 db + i at tile rows 16 kc + 8 (e / 4) + 4 g + (e mod 4),
 // e = 0..7 — the order of the k slots in a 32x32 accumulator's lane.
-__device__ __forceinline__ bf16x8 trans_frag(const u16* t, int lane, int db, int kc) {
+template <typename T>
+__device__ __forceinline__ typename Fmt16<T>::v8 trans_frag(const u16* t, int lane, int db,
+                                                            int kc) {
   const int tq = lane >> 4, tl = lane & 15;
   const int col = 32 * db + 16 * (tq & 1) + 4 * (tl & 3);
   const int row = 16 * kc + 4 * (tq >> 1) + (tl >> 2);
@@ -75,13 +81,14 @@ __device__ __forceinline__ bf16x8 trans_frag(const u16* t, int lane, int db, int
   const s16x4 hi = lds_read_tr16(&t[tile_off(row + 8, col)]);
   const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
   const u32x4 vv = {lo2[0], lo2[1], hi2[0], hi2[1]};
-  return __builtin_bit_cast(bf16x8, vv);
+  return __builtin_bit_cast(typename Fmt16<T>::v8, vv);
 }
 
 // Stores a 32-column block of a transposed accumulator pair acc[db] (rows d,
-// columns = this lane's row of the output) as bf16: lane (c, g) holds
+// columns = this lane's row of the output) in the format T: lane (c, g) holds
 // d = 32 db + 8 a + 4 g + e for a, e < 4.  With tab non-null the pairs
 // (d, d+1) are rotated back (R^T at the table row given) in fp64.
+template <typename T>
 __device__ __forceinline__ void store_row(u16* out, const f32x16* acc, float mul, int g,
                                           const double2* tabrow) {
 #pragma unroll
@@ -100,11 +107,11 @@ __device__ __forceinline__ void store_row(u16* out, const f32x16* acc, float mul
           const double x0 = x[2 * pr], x1 = x[2 * pr + 1];
           const double r0 = x0 * cs.x + x1 * cs.y;
           const double r1 = -x0 * cs.y + x1 * cs.x;
-          pk[pr] = f64_to_bf16_bits(r0) | (f64_to_bf16_bits(r1) << 16);
+          pk[pr] = Fmt16<T>::from_f64(r0) | (Fmt16<T>::from_f64(r1) << 16);
         }
       } else {
-        pk[0] = pack_bf16(x[0], x[1]);
-        pk[1] = pack_bf16(x[2], x[3]);
+        pk[0] = Fmt16<T>::pack(x[0], x[1]);
+        pk[1] = Fmt16<T>::pack(x[2], x[3]);
       }
       *reinterpret_cast<u32x2*>(out + d) = pk;
     }
@@ -114,13 +121,14 @@ __device__ __forceinline__ void store_row(u16* out, const f32x16* acc, float mul
 
 // ---------------------------------------------------------------- prep --
 
+template <typename T>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const u16* __restrict__ O,
                                                        const u16* __restrict__ dO,
                                                        const float* __restrict__ lse,
                                                        float* __restrict__ delta,
                                                        float* __restrict__ lse2, int B, int Sq,
                                                        int Hq) {
-  // 8 lanes per (b, i, h) row of 64 bf16, rows in [B, Sq, Hq] order
+  // 8 lanes per (b, i, h) row of 64 16-bit values, rows in [B, Sq, Hq] order
   const long long row = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int part = threadIdx.x & 7;
   const long long nrows = (long long)B * Sq * Hq;
@@ -130,8 +138,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const u16* __restrict__ O
     const u32x4 c = *reinterpret_cast<const u32x4*>(dO + row * kD + part * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc = fmaf(bf16_lo(a[e]), bf16_lo(c[e]), acc);
-      acc = fmaf(bf16_hi(a[e]), bf16_hi(c[e]), acc);
+      acc = fmaf(Fmt16<T>::lo(a[e]), Fmt16<T>::lo(c[e]), acc);
+      acc = fmaf(Fmt16<T>::hi(a[e]), Fmt16<T>::hi(c[e]), acc);
     }
   }
   acc = group_sum<8>(acc);
@@ -149,7 +157,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const u16* __restrict__ O
 
 // ---------------------------------------------------------------- dK, dV --
 
-template <bool CAUSAL, bool ROPE>
+template <typename T, bool CAUSAL, bool ROPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
@@ -158,6 +166,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int D = kD, BQ = 64, BK = 128, NKS = D / 16;
   constexpr int LD = BQ * kKCH / 256;  // direct loads per thread per tile and tensor
   static_assert(LD == 2, "layout assumed below");
+  typedef Fmt16<T> F;
+  typedef typename F::v8 v8;
 
   __shared__ __attribute__((aligned(16))) u16 Qs0[BQ * D];
   __shared__ __attribute__((aligned(16))) u16 Os0[BQ * D];  // dO
@@ -180,7 +190,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // K and V of the wave's 32 keys as B operands: lane (c, g), k-step ks holds
   // columns 16 ks + 8 g .. +7 of key `key`; keys past Skv are zero.
-  bf16x8 kf[NKS], vf[NKS];
+  v8 kf[NKS], vf[NKS];
   {
     const bool ok = key < Skv;
     const long long base = (((long long)b * Skv + (ok ? key : 0)) * Hkv + kvh) * D + g * 8;
@@ -191,8 +201,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         a = *reinterpret_cast<const u32x4*>(K + base + 16 * ks);
         v = *reinterpret_cast<const u32x4*>(V + base + 16 * ks);
       }
-      kf[ks] = __builtin_bit_cast(bf16x8, a);
-      vf[ks] = __builtin_bit_cast(bf16x8, v);
+      kf[ks] = __builtin_bit_cast(v8, a);
+      vf[ks] = __builtin_bit_cast(v8, v);
     }
   }
 
@@ -269,10 +279,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_frag(qs, 32 * qb, c, g, ks), kf[ks],
-                                                        s[qb], 0, 0, 0);
-        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_frag(os, 32 * qb, c, g, ks),
-                                                         vf[ks], dp[qb], 0, 0, 0);
+        s[qb] = F::mfma(rows_frag<T>(qs, 32 * qb, c, g, ks), kf[ks], s[qb]);
+        dp[qb] = F::mfma(rows_frag<T>(os, 32 * qb, c, g, ks), vf[ks], dp[qb]);
       }
 
     // P = exp2(c s - lse2) in place of S; lane holds tile rows
@@ -296,8 +304,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int r = 0; r < 16; ++r)
           if (key > p0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3) + off) s[qb][r] = 0.f;
     }
-    // dS = P (dP - D); P and dS as bf16 B operands
-    bf16x8 pf[4], sf[4];
+    // dS = P (dP - D); P and dS as 16-bit B operands
+    v8 pf[4], sf[4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -307,8 +315,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * a + e;
           // k slot r of query block qb: chunk 2 qb + r / 8, element r mod 8
-          pf[2 * qb + r / 8][r % 8] = (__bf16)s[qb][r];
-          sf[2 * qb + r / 8][r % 8] = (__bf16)(s[qb][r] * (dp[qb][r] - d4[e]));
+          pf[2 * qb + r / 8][r % 8] = (T)s[qb][r];
+          sf[2 * qb + r / 8][r % 8] = (T)(s[qb][r] * (dp[qb][r] - d4[e]));
         }
       }
 
@@ -317,10 +325,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag(os, lane, db, kc), pf[kc],
-                                                            dvacc[db], 0, 0, 0);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag(qs, lane, db, kc), sf[kc],
-                                                            dkacc[db], 0, 0, 0);
+        dvacc[db] = F::mfma(trans_frag<T>(os, lane, db, kc), pf[kc], dvacc[db]);
+        dkacc[db] = F::mfma(trans_frag<T>(qs, lane, db, kc), sf[kc], dkacc[db]);
       }
   };
 
@@ -349,14 +355,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   if (key < Skv) {
     const long long orow = (((long long)b * Skv + key) * Hkv + kvh) * D;
-    store_row(dV + orow, dvacc, 1.f, g, nullptr);
-    store_row(dK + orow, dkacc, scale, g, ROPE ? tab + (long long)key * (D / 2) : nullptr);
+    store_row<T>(dV + orow, dvacc, 1.f, g, nullptr);
+    store_row<T>(dK + orow, dkacc, scale, g, ROPE ? tab + (long long)key * (D / 2) : nullptr);
   }
 }
 
 // ---------------------------------------------------------------- dQ --
 
-template <int HPW, bool CAUSAL, bool ROPE>
+template <typename T, int HPW, bool CAUSAL, bool ROPE>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
@@ -365,6 +371,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   constexpr int D = kD, BM = 128, BN = 64, NP = BM / HPW, NKS = D / 16;
   constexpr int LD = BN * kKCH / 256;
   static_assert(LD == 2, "layout assumed below");
+  typedef Fmt16<T> F;
+  typedef typename F::v8 v8;
 
   __shared__ __attribute__((aligned(16))) u16 Ks0[BN * D];
   __shared__ __attribute__((aligned(16))) u16 Vs0[BN * D];
@@ -389,7 +397,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   const bool qvalid = pos < Sq;
   const int qlim = CAUSAL ? min(pos + off, Skv - 1) : Skv - 1;
 
-  bf16x8 qf[NKS], of[NKS];
+  v8 qf[NKS], of[NKS];
   float l2 = INFINITY, dl = 0.f;
   {
     const long long base = (((long long)b * Sq + (qvalid ? pos : 0)) * Hq + hh) * D + g * 8;
@@ -400,8 +408,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
         a = *reinterpret_cast<const u32x4*>(Q + base + 16 * ks);
         o = *reinterpret_cast<const u32x4*>(dO + base + 16 * ks);
       }
-      qf[ks] = __builtin_bit_cast(bf16x8, a);
-      of[ks] = __builtin_bit_cast(bf16x8, o);
+      qf[ks] = __builtin_bit_cast(v8, a);
+      of[ks] = __builtin_bit_cast(v8, o);
     }
     if (qvalid) {
       const long long st = ((long long)b * Hq + hh) * Sq + pos;
@@ -452,10 +460,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_frag(ks_, 32 * kb, c, g, ks),
-                                                        qf[ks], s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_frag(vs_, 32 * kb, c, g, ks),
-                                                         of[ks], dp[kb], 0, 0, 0);
+        s[kb] = F::mfma(rows_frag<T>(ks_, 32 * kb, c, g, ks), qf[ks], s[kb]);
+        dp[kb] = F::mfma(rows_frag<T>(vs_, 32 * kb, c, g, ks), of[ks], dp[kb]);
       }
     // P^T in place of S^T; lane holds keys k0 + 32 kb + 8 a + 4 g + e of its
     // query.  Keys at or past Skv need no mask here: their K rows read as
@@ -473,19 +479,18 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
         for (int r = 0; r < 16; ++r)
           if (k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) > qlim) s[kb][r] = 0.f;
     }
-    // dS^T = P^T (dP^T - D) as bf16 B operands
-    bf16x8 sf[4];
+    // dS^T = P^T (dP^T - D) as 16-bit B operands
+    v8 sf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sf[2 * kb + r / 8][r % 8] = (__bf16)(s[kb][r] * (dp[kb][r] - dl));
+      for (int r = 0; r < 16; ++r) sf[2 * kb + r / 8][r % 8] = (T)(s[kb][r] * (dp[kb][r] - dl));
     // dQ^T += K^T dS^T (rows d, columns queries)
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
       for (int db = 0; db < 2; ++db)
-        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag(ks_, lane, db, kc), sf[kc],
-                                                            dqacc[db], 0, 0, 0);
+        dqacc[db] = F::mfma(trans_frag<T>(ks_, lane, db, kc), sf[kc], dqacc[db]);
   };
 
   if (ntiles > 0) dma(0, Ks0, Vs0);
@@ -504,7 +509,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   }
 
   if (qvalid)
-    store_row(dQ + (((long long)b * Sq + pos) * Hq + hh) * D, dqacc, scale, g,
+    store_row<T>(dQ + (((long long)b * Sq + pos) * Hq + hh) * D, dqacc, scale, g,
               ROPE ? tab + (long long)(off + pos) * (D / 2) : nullptr);
 }
 
@@ -512,7 +517,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 
 namespace {
 
-template <bool C, bool R>
+template <typename T, bool C, bool R>
 hipError_t go_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                   const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
                   int Skv, float scale, const double2* tab, float* delta, float* lse2,
@@ -526,7 +531,7 @@ hipError_t go_bwd(const void* q, const void* k, const void* v, const void* o, co
   const long long nrows = (long long)B * Sq * Hq;
   const long long nprep = (nrows + 31) / 32;
   if (nprep > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  bwd_prep_kernel<<<dim3((unsigned)nprep), dim3(256), 0, stream>>>(
+  bwd_prep_kernel<T><<<dim3((unsigned)nprep), dim3(256), 0, stream>>>(
       static_cast<const u16*>(o), dO, lse, delta, lse2, B, Sq, Hq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -534,7 +539,7 @@ hipError_t go_bwd(const void* q, const void* k, const void* v, const void* o, co
   const int n_bh_kv = B * Hkv;
   const long long nkv = (long long)((Skv + 127) / 128) * n_bh_kv;
   if (nkv > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  bwd_dkdv_kernel<C, R><<<dim3((unsigned)nkv), dim3(256), 0, stream>>>(
+  bwd_dkdv_kernel<T, C, R><<<dim3((unsigned)nkv), dim3(256), 0, stream>>>(
       Q, Kp, Vp, dO, lse2, delta, static_cast<u16*>(dk), static_cast<u16*>(dv), Hq, Hkv, Sq, Skv,
       scale, sl2, tab, n_bh_kv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -547,7 +552,7 @@ hipError_t go_bwd(const void* q, const void* k, const void* v, const void* o, co
     const int n_bh = B * (Hq / HPW);
     const long long nb = (long long)n_qt * n_bh;
     if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    bwd_dq_kernel<HPW, C, R><<<dim3((unsigned)nb), dim3(256), 0, stream>>>(
+    bwd_dq_kernel<T, HPW, C, R><<<dim3((unsigned)nb), dim3(256), 0, stream>>>(
         Q, Kp, Vp, dO, lse2, delta, static_cast<u16*>(dq), Hq, Hkv, Sq, Skv, scale, sl2, tab,
         n_qt, n_bh);
     return hipGetLastError();
@@ -566,12 +571,11 @@ size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D, bool 
   return n;
 }
 
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
-                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
-                           float scale, const double2* rope_tab, void* workspace,
-                           hipStream_t stream) {
-  if (D != kD) return hipErrorInvalidValue;
+hipError_t launch_bwd16(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                        int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                        const double2* rope_tab, int dtype, void* workspace, hipStream_t stream) {
+  if (D != kD || (dtype != 1 && dtype != 2)) return hipErrorInvalidValue;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   char* ws = static_cast<char*>(workspace);
   float* delta = reinterpret_cast<float*>(ws);
@@ -584,21 +588,28 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
     char* ks = qs + up((size_t)B * Sq * Hq * D * 2);
     // queries at positions Skv - Sq + i: table rows from Skv - Sq on
     hipError_t e = launch_rope_rotate(q, qs, B, Sq, Hq, D, rope_tab + (size_t)(Skv - Sq) * (D / 2),
-                                      1, stream);
+                                      dtype, stream);
     if (e != hipSuccess) return e;
-    e = launch_rope_rotate(k, ks, B, Skv, Hkv, D, rope_tab, 1, stream);
+    e = launch_rope_rotate(k, ks, B, Skv, Hkv, D, rope_tab, dtype, stream);
     if (e != hipSuccess) return e;
     qin = qs;
     kin = ks;
   }
-#define XATTN_BWD_CASE(C, R)                                                                  \
-  if ((causal != 0) == C && rope == R)                                                        \
-    return go_bwd<C, R>(qin, kin, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, scale,   \
-                        rope_tab, delta, lse2, stream);
-  XATTN_BWD_CASE(false, false)
-  XATTN_BWD_CASE(true, false)
-  XATTN_BWD_CASE(false, true)
-  XATTN_BWD_CASE(true, true)
+#define XATTN_BWD_CASE(TT, C, R)                                                               \
+  if ((causal != 0) == C && rope == R)                                                         \
+    return go_bwd<TT, C, R>(qin, kin, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, scale, \
+                            rope_tab, delta, lse2, stream);
+  if (dtype == 1) {
+    XATTN_BWD_CASE(__bf16, false, false)
+    XATTN_BWD_CASE(__bf16, true, false)
+    XATTN_BWD_CASE(__bf16, false, true)
+    XATTN_BWD_CASE(__bf16, true, true)
+  } else {
+    XATTN_BWD_CASE(_Float16, false, false)
+    XATTN_BWD_CASE(_Float16, true, false)
+    XATTN_BWD_CASE(_Float16, false, true)
+    XATTN_BWD_CASE(_Float16, true, true)
+  }
 #undef XATTN_BWD_CASE
   return hipErrorInvalidValue;
 }

@@ -51,16 +51,16 @@ hipError_t launch_rope_table(double2* tab, int pos0, int npos, int D, double bas
 hipError_t launch_rope_rotate(const void* x, void* y, int B, int S, int H, int D,
                               const double2* tab, int dtype, hipStream_t stream);
 
-// Backward (bf16, D = 64): q, k, v, o, dout like the forward's tensors, lse its
-// [B,Hq,Sq] output; dq like q, dk and dv like k.  rope_tab: table rows for
-// positions [0, Skv) (null: no RoPE).  workspace: bwd_workspace_bytes bytes
-// (per-row D and log2 lse, then, with RoPE, the rotated Q and K).
+// Backward (16-bit: dtype 1 bf16, 2 fp16; D = 64): q, k, v, o, dout like the
+// forward's tensors, lse its [B,Hq,Sq] output; dq like q, dk and dv like k.
+// rope_tab: table rows for positions [0, Skv) (null: no RoPE).  workspace:
+// bwd_workspace_bytes bytes (per-row D and log2 lse, then, with RoPE, the
+// rotated Q and K).
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D, bool rope);
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
-                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
-                           float scale, const double2* rope_tab, void* workspace,
-                           hipStream_t stream);
+hipError_t launch_bwd16(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                        int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                        const double2* rope_tab, int dtype, void* workspace, hipStream_t stream);
 
 // Head dims other than 64/128: copy x [B,S,H,D] into y [B,S,H,Dp] with zero
 // columns past D (dtype 0 fp32 / 1 bf16 / 2 fp16), rotating pair i < D/2 of token t by

@@ -147,9 +147,9 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D, 
  *   dk~[b,j,g,:] = scale sum over h in group g and rows i of dS_ij q~[b,i,h,:]
  *   dq = R^T dq~, dk = R^T dk~  (R: the forward's rotation at the same
  *   positions; identity without RoPE)
- * P and dS enter the MFMA contractions as bf16; accumulation is fp32 and the
- * inverse rotation fp64.  Deterministic: no atomics, the same inputs give the
- * same bits.
+ * P and dS enter the MFMA contractions in the input format (bf16 or fp16);
+ * accumulation is fp32 and the inverse rotation fp64.  Deterministic: no
+ * atomics, the same inputs give the same bits.
  *
  * Arguments:
  *   q, k, v, causal, scale, rope_base, dtype: as given to attn_fwd
@@ -159,7 +159,7 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D, 
  *   dq   [B, Sq, Hq, D] dtype, dk and dv [B, Skv, Hkv, D] dtype (outputs)
  *   workspace: attn_bwd_workspace_bytes(...) bytes of device memory, or NULL
  *          to use a library-owned buffer
- *   Built: dtype ATTN_BF16 with D == 64; RoPE needs Sq <= Skv.
+ *   Built: dtype ATTN_BF16 or ATTN_F16 with D == 64; RoPE needs Sq <= Skv.
  * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED (other dtype or D),
  *   ATTN_ERR_EMPTY_KV (Skv == 0), ATTN_ERR_HIP.
  */

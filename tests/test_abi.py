@@ -164,7 +164,7 @@ def _bwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAK
     (dict(D=63, rope=100.0), xa.ATTN_ERR_INVALID),
     (dict(dtype=9), xa.ATTN_ERR_INVALID),
     (dict(dtype=0), xa.ATTN_ERR_UNSUPPORTED),
-    (dict(dtype=2), xa.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=2, D=128), xa.ATTN_ERR_UNSUPPORTED),
     (dict(D=128), xa.ATTN_ERR_UNSUPPORTED),
     (dict(Sq=16, Skv=8, rope=10000.0), xa.ATTN_ERR_UNSUPPORTED),
 ])

@@ -1,5 +1,5 @@
-"""GPU parity for IEEE binary16 (fp16) inputs: attn_fwd, attn_fwd_masked and
-rope_apply with dtype fp16, through the C ABI, against the fp64 oracle fed the
+"""GPU parity for IEEE binary16 (fp16) inputs: attn_fwd, attn_fwd_masked,
+attn_bwd and rope_apply with dtype fp16, through the C ABI, against the fp64 oracle fed the
 same fp16 values (widened exactly; rotated q and k rounded to fp16, as the
 kernels do).
 
@@ -145,11 +145,44 @@ def test_rope_apply_f16(D, off):
     assert (got == ref).mean() > 0.9999
 
 
+BWD16_CASES = [  # B, Hq, Hkv, Sq, Skv, causal, rope
+    (2, 8, 2, 300, 300, True, 10000.0),    # GQA 4, RoPE, ragged tiles
+    (1, 4, 4, 200, 333, False, 0.0),       # MHA, Sq != Skv
+    (1, 4, 1, 100, 260, True, 10000.0),    # bottom-right causal, Sq < Skv
+    (1, 12, 4, 97, 150, True, 0.0),        # 3 query heads per kv head
+]
+
+
+@pytest.mark.parametrize("case", BWD16_CASES, ids=[str(c) for c in BWD16_CASES])
+def test_f16_backward(case):
+    """attn_bwd on fp16 inputs (P and dS enter the MFMAs as fp16) against the
+    oracle's gradients of the same fp16 values, with the bf16 backward's bar:
+    per tensor rel-L2 <= 1e-2 and max-abs <= 2e-2 max |ref| (fp16's rounding
+    is 8 times finer, so this holds with a wide margin)."""
+    from test_gpu_backward import check_grad
+    B, Hq, Hkv, Sq, Skv, causal, rope = case
+    D = 64
+    say("case f16 bwd", case)
+    rng = np.random.default_rng(abs(hash(case)) % 2 ** 32)
+    q, k, v = _inputs(rng, B, Hq, Hkv, Sq, Skv, D)
+    do = rng.standard_normal((B, Sq, Hq, D), dtype=np.float32).astype(np.float16)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    qd, kd, vd, dod = (W.to_device(x) for x in (q, k, v, do))
+    o, lse = xa.attn_fwd(qd, kd, vd, causal=causal, scale=scale, rope_base=rope)
+    dq, dk, dv = xa.attn_bwd(qd, kd, vd, o, dod, lse, causal=causal, scale=scale, rope_base=rope)
+    assert dq.dtype == torch.float16
+    torch.cuda.synchronize()
+    ref = oracle.attn_bwd(q, k, v, do, causal=causal, scale=scale, rope_base=rope,
+                          nthreads=NTHREADS)
+    for g, r, n in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+        check_grad(_np(g), r, f"f16 {case} {n}")
+
+
 def test_f16_unsupported_paths():
-    """Paths built for bf16 only refuse fp16 with ATTN_ERR_UNSUPPORTED."""
-    q = torch.zeros(1, 8, 4, 64, dtype=torch.float16, device="cuda")
-    k = torch.zeros(1, 8, 4, 64, dtype=torch.float16, device="cuda")
-    o, lse = xa.attn_fwd(q, k, k)
-    with pytest.raises(xa.AttnError) as e:
-        xa.attn_bwd(q, k, k, o, o, lse)
-    assert e.value.code == xa.ATTN_ERR_UNSUPPORTED
+    """fp32 and D = 128 have no backward: ATTN_ERR_UNSUPPORTED."""
+    for dt, D in ((torch.float32, 64), (torch.float16, 128)):
+        q = torch.zeros(1, 8, 4, D, dtype=dt, device="cuda")
+        o, lse = xa.attn_fwd(q, q, q)
+        with pytest.raises(xa.AttnError) as e:
+            xa.attn_bwd(q, q, q, o, o, lse)
+        assert e.value.code == xa.ATTN_ERR_UNSUPPORTED

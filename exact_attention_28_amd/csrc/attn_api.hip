@@ -44,6 +44,12 @@ int ok() {
 struct DevBuffers {
   void* rope_tab = nullptr;
   size_t rope_tab_bytes = 0;
+  // what the RoPE table holds: positions [tab_pos0, tab_pos0 + tab_npos) for
+  // head dim tab_D and base tab_base, written on tab_stream
+  bool tab_ok = false;
+  int tab_pos0 = 0, tab_npos = 0, tab_D = 0;
+  double tab_base = 0.0;
+  hipStream_t tab_stream = nullptr;
   void* kstage = nullptr;
   size_t kstage_bytes = 0;
   void* dec_ws = nullptr;
@@ -93,6 +99,35 @@ int hip_status(hipError_t e, const char* what) {
   return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// The fp64 (cos, sin) table for positions [pos0, pos0 + npos) at head dim D
+// (caller holds g_mu).  A table built earlier on the same stream for the same
+// first position, D and base that covers npos positions is reused (its values
+// are the same; stream order puts its build before this call's kernels);
+// otherwise the table is rebuilt on `stream`.
+int rope_table(DevBuffers* db, int pos0, int npos, int D, float base, hipStream_t stream,
+               const double2** tab, const char* fn) {
+  if (db->tab_ok && db->tab_stream == stream && db->tab_pos0 == pos0 && db->tab_D == D &&
+      db->tab_base == (double)base && db->tab_npos >= npos) {
+    *tab = static_cast<const double2*>(db->rope_tab);
+    return ATTN_OK;
+  }
+  db->tab_ok = false;
+  const size_t bytes = (size_t)npos * (D / 2) * sizeof(double2);
+  int st = grow(&db->rope_tab, &db->rope_tab_bytes, bytes, "rope table");
+  if (st != ATTN_OK) return st;
+  hipError_t e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), pos0, npos, D,
+                                          (double)base, stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: rope table launch: %s", fn, hipGetErrorString(e));
+  db->tab_ok = true;
+  db->tab_pos0 = pos0;
+  db->tab_npos = npos;
+  db->tab_D = D;
+  db->tab_base = (double)base;
+  db->tab_stream = stream;
+  *tab = static_cast<const double2*>(db->rope_tab);
+  return ATTN_OK;
+}
+
 // attn_fwd for a head dim other than 64 and 128: zero-padded copies of Q, K,
 // V (Q and K rotated with the angles of the true D), the kernel at the padded
 // width without rotation, then O's first D columns.
@@ -114,15 +149,9 @@ int fwd_padded(const void* q, const void* k, const void* v, void* o, float* lse,
   void *qp = base, *kp = base + qb, *vp = base + qb + kb, *op = base + qb + 2 * kb;
   const double2* tab = nullptr;
   hipError_t e;
-  if (rope_base > 0.f) {
-    const size_t tab_bytes = (size_t)Skv * (D / 2) * sizeof(double2);
-    if ((st = grow(&db->rope_tab, &db->rope_tab_bytes, tab_bytes, "rope table")) != ATTN_OK)
-      return st;
-    tab = static_cast<const double2*>(db->rope_tab);
-    e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), 0, Skv, D,
-                                 (double)rope_base, stream);
-    if (e != hipSuccess) return hip_status(e, "attn_fwd: rope table launch");
-  }
+  if (rope_base > 0.f &&
+      (st = rope_table(db, 0, Skv, D, rope_base, stream, &tab, "attn_fwd")) != ATTN_OK)
+    return st;
   const int dt = dtype;  // kernel format codes: 0 fp32, 1 bf16, 2 fp16
   if ((e = xattn::launch_pack_heads(q, qp, B, Sq, Hq, D, Dp, tab, Skv - Sq, dt, stream)) !=
           hipSuccess ||
@@ -178,13 +207,8 @@ int fwd(const char* fn, const void* q, const void* k, const void* v, void* o, fl
     int st;
     DevBuffers* db = buffers(&st);
     if (!db) return st;
-    const size_t tab_bytes = (size_t)Skv * (D / 2) * sizeof(double2);
-    if ((st = grow(&db->rope_tab, &db->rope_tab_bytes, tab_bytes, "rope table")) != ATTN_OK)
-      return st;
-    tab = static_cast<const double2*>(db->rope_tab);
-    hipError_t e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), 0, Skv, D,
-                                            (double)rope_base, stream);
-    if (e != hipSuccess) return hip_status(e, "attn_fwd: rope table launch");
+    if ((st = rope_table(db, 0, Skv, D, rope_base, stream, &tab, fn)) != ATTN_OK) return st;
+    hipError_t e;
     if (dtype != ATTN_F32) {
       const size_t kb = (size_t)B * Skv * Hkv * D * 2;
       if ((st = grow(&db->kstage, &db->kstage_bytes, kb, "rotated K")) != ATTN_OK) return st;
@@ -276,15 +300,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   DevBuffers* db = buffers(&st);
   if (!db) return st;
   const double2* tab = nullptr;
-  if (rope) {
-    const size_t tab_bytes = (size_t)Skv * (D / 2) * sizeof(double2);
-    if ((st = grow(&db->rope_tab, &db->rope_tab_bytes, tab_bytes, "rope table")) != ATTN_OK)
-      return st;
-    tab = static_cast<const double2*>(db->rope_tab);
-    hipError_t e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), 0, Skv, D,
-                                            (double)rope_base, stream);
-    if (e != hipSuccess) return hip_status(e, "attn_bwd: rope table launch");
-  }
+  if (rope && (st = rope_table(db, 0, Skv, D, rope_base, stream, &tab, "attn_bwd")) != ATTN_OK)
+    return st;
   void* ws = workspace;
   if (ws == nullptr) {
     if ((st = grow(&db->bwd_ws, &db->bwd_ws_bytes,
@@ -379,13 +396,9 @@ int attn_prefill_kvcache(const void* q, const void* k_new, const void* v_new, vo
     int st;
     DevBuffers* db = buffers(&st);
     if (!db) return st;
-    const size_t tab_bytes = (size_t)max_seqlen * (D / 2) * sizeof(double2);
-    if ((st = grow(&db->rope_tab, &db->rope_tab_bytes, tab_bytes, "rope table")) != ATTN_OK)
+    if ((st = rope_table(db, 0, max_seqlen, D, rope_base, stream, &tab, "attn_prefill_kvcache")) !=
+        ATTN_OK)
       return st;
-    tab = static_cast<const double2*>(db->rope_tab);
-    hipError_t e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), 0, max_seqlen, D,
-                                            (double)rope_base, stream);
-    if (e != hipSuccess) return hip_status(e, "attn_prefill_kvcache: rope table launch");
   }
   hipError_t e = xattn::launch_cache_append(k_new, v_new, kcache, vcache, cache_lens, B, Sq, Hkv,
                                             D, max_seqlen, tab, stream);
@@ -412,14 +425,10 @@ int rope_apply(void* x, int B, int S, int H, int D, int pos_offset, float rope_b
   int st;
   DevBuffers* db = buffers(&st);
   if (!db) return st;
-  const size_t tab_bytes = (size_t)S * (D / 2) * sizeof(double2);
-  if ((st = grow(&db->rope_tab, &db->rope_tab_bytes, tab_bytes, "rope table")) != ATTN_OK)
+  const double2* tab = nullptr;
+  if ((st = rope_table(db, pos_offset, S, D, rope_base, stream, &tab, "rope_apply")) != ATTN_OK)
     return st;
-  hipError_t e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), pos_offset, S, D,
-                                          (double)rope_base, stream);
-  if (e != hipSuccess) return hip_status(e, "rope_apply: table launch");
-  e = xattn::launch_rope_rotate(x, x, B, S, H, D, static_cast<const double2*>(db->rope_tab),
-                                dtype, stream);
+  hipError_t e = xattn::launch_rope_rotate(x, x, B, S, H, D, tab, dtype, stream);
   return hip_status(e, "rope_apply: kernel launch");
 }
 

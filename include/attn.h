@@ -27,6 +27,10 @@
  *    decode and backward workspaces) are allocated on first need, grow only, and are kept per
  *    device until the process ends; calls that use them concurrently on
  *    different streams of one device must be ordered by the caller.
+ *  - The fp64 RoPE (cos, sin) table is built on the call's stream when a call
+ *    needs positions, a head dim or a base that the table does not hold, or
+ *    runs on another stream than the one that built it; otherwise it is
+ *    reused (the same values, ordered before the call by its stream).
  */
 #ifndef EXACT_ATTN_H
 #define EXACT_ATTN_H
@@ -236,7 +240,8 @@ int attn_decode_splitkv(const void* q, const void* kcache, const void* vcache,
  *   B, Hq, Hkv, Sq >= 1; Hq % Hkv == 0; D in {64, 128}; 1 <= Sq <= max_seqlen;
  *   causal 0 or 1; scale finite and > 0; rope_base > 0 enables RoPE (D even)
  * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP.  With RoPE the
- *   call rebuilds the library's RoPE table for max_seqlen positions.
+ *   call uses the library's RoPE table for max_seqlen positions (built on the
+ *   first such call on a stream and reused by the next ones).
  */
 int attn_prefill_kvcache(const void* q, const void* k_new, const void* v_new, void* kcache,
                          void* vcache, const int* cache_lens, void* o, float* lse, int B, int Hq,

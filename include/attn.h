@@ -96,7 +96,7 @@ typedef enum {
  *          accumulation; P enters the second product in the input format), or
  *          ATTN_F32 (fp32 throughout)
  * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_EMPTY_KV (Skv == 0),
- *   ATTN_ERR_HIP.  With rope_base > 0 and bf16, the call may allocate the
+ *   ATTN_ERR_HIP.  With rope_base > 0 and a 16-bit dtype, the call may allocate the
  *   library's rotated-K staging buffer (B*Skv*Hkv*D*2 bytes) and RoPE table.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
@@ -130,7 +130,7 @@ int attn_fwd_masked(const void* q, const void* k, const void* v, const float* ma
 /*
  * attn_bwd_workspace_bytes — size of the workspace attn_bwd needs: the per-row
  * D_i and log2 lse ([B, Hq, Sq] fp32 each) and, with rope_base > 0, the rotated
- * Q and K (B*Sq*Hq*D and B*Skv*Hkv*D bf16), each part rounded up to 256 bytes.
+ * Q and K (B*Sq*Hq*D and B*Skv*Hkv*D 16-bit values), each part rounded up to 256 bytes.
  * Returns 0 for invalid sizes.
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D, float rope_base);

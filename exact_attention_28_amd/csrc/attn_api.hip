@@ -196,6 +196,10 @@ int fwd(const char* fn, const void* q, const void* k, const void* v, void* o, fl
                 "%s: RoPE with Sq > Skv would place queries at negative positions", fn);
   if ((long long)B * Hq * ((Sq + 15) / 16) > 0x7fffffffLL || B > 65535 || Hq > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  // the 16-bit kernels address one batch's K and V (at their 64- or 128-wide
+  // rows) through 32-bit buffer offsets
+  if (dtype != ATTN_F32 && (long long)Skv * Hkv * (D <= 64 ? 64 : 128) * 2 >= 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: one batch's K or V exceeds 2 GiB", fn);
   if (D != 64 && D != 128)
     return fwd_padded(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, rope_base, dtype,
                       mask, stream);

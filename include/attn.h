@@ -95,7 +95,9 @@ typedef enum {
  *   dtype: ATTN_BF16 or ATTN_F16 (16-bit MFMA of that format, fp32
  *          accumulation; P enters the second product in the input format), or
  *          ATTN_F32 (fp32 throughout)
- * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_EMPTY_KV (Skv == 0),
+ * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED (also for 16-bit inputs whose
+ *   one batch of K or V, at 64 or 128 columns, reaches 2 GiB: the kernels use
+ *   32-bit buffer offsets), ATTN_ERR_EMPTY_KV (Skv == 0),
  *   ATTN_ERR_HIP.  With rope_base > 0 and a 16-bit dtype, the call may allocate the
  *   library's rotated-K staging buffer (B*Skv*Hkv*D*2 bytes) and RoPE table.
  */

@@ -63,6 +63,8 @@ def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=4, Hkv=2, Sq=8, 
     (dict(D=63, rope=10000.0, dtype=2), xa.ATTN_ERR_INVALID),
     (dict(D=256), xa.ATTN_ERR_UNSUPPORTED),
     (dict(Sq=16, Skv=8, rope=10000.0), xa.ATTN_ERR_UNSUPPORTED),
+    (dict(Skv=1 << 21, Hkv=8, Hq=8), xa.ATTN_ERR_UNSUPPORTED),           # 2 GiB of K per batch
+    (dict(Skv=1 << 21, Hkv=8, Hq=8, D=40, dtype=2), xa.ATTN_ERR_UNSUPPORTED),  # padded to 64
 ])
 def test_attn_fwd_validation(lib, kw, code):
     assert _fwd(lib, **kw) == code
@@ -89,6 +91,7 @@ def _fwdm(lib, mask=FAKE, bs=0, hs=0, rs=8, **kw):
     (dict(scale=0.0), xa.ATTN_ERR_INVALID),
     (dict(D=256), xa.ATTN_ERR_UNSUPPORTED),
     (dict(dtype=5), xa.ATTN_ERR_INVALID),
+    (dict(Skv=1 << 21, Hkv=8, Hq=8), xa.ATTN_ERR_UNSUPPORTED),
 ])
 def test_attn_fwd_masked_validation(lib, kw, code):
     assert _fwdm(lib, **kw) == code

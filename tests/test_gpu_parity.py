@@ -361,3 +361,27 @@ def test_padded_head_dims(case):
         check_f32(o, lse, o_ref, lse_ref, str(case))
     else:
         check_bf16(o, lse, o_ref, lse_ref, str(case))
+
+
+def test_keys_up_to_the_32bit_offset_limit():
+    """One batch of K and V just under 2 GiB each (7 999 488 keys, D = 128,
+    one kv head): the 16-bit kernel's 32-bit buffer offsets reach their
+    largest values.  The keys are one random 4096-key block repeated 1953
+    times, so O equals the block's attention and the LSE is the block's plus
+    ln 1953 (every weight repeated n times); the oracle evaluates the block."""
+    reps, blk, D = 1953, 4096, 128
+    say("case 32-bit offset limit", reps * blk)
+    rng = np.random.default_rng(77)
+    q = W.f32_to_bf16_bits(rng.standard_normal((1, 4, 2, D), dtype=np.float32))
+    kb = W.f32_to_bf16_bits(rng.standard_normal((1, blk, 1, D), dtype=np.float32))
+    vb = W.f32_to_bf16_bits(rng.standard_normal((1, blk, 1, D), dtype=np.float32))
+    kd = W.to_device(kb).repeat(1, reps, 1, 1)
+    vd = W.to_device(vb).repeat(1, reps, 1, 1)
+    assert kd.numel() * 2 < 2 ** 31
+    scale = float(np.float32(1 / math.sqrt(D)))
+    o, lse = xa.attn_fwd(W.to_device(q), kd, vd, causal=False, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(q, kb, vb, causal=False, scale=scale)
+    check_bf16(_np(o), _np(lse), o_ref, lse_ref + math.log(reps), "8M keys")
+    del kd, vd
+    torch.cuda.empty_cache()

@@ -134,6 +134,10 @@ BF16_CASES = [  # B, Hq, Hkv, Sq, Skv, D, causal, rope, amplitude
     (1, 16, 2, 129, 129, 64, True, 10000.0, 1.0),  # 8 query heads per kv head
     (2, 5, 5, 64, 64, 128, True, 0.0, 1.0),
     (1, 12, 4, 97, 97, 64, False, 0.0, 1.0),    # 3 query heads per kv head
+    (2, 8, 2, 1, 777, 64, True, 10000.0, 1.0),  # one query row against every key
+    (1, 4, 2, 256, 320, 64, True, 0.0, 4.0),    # scores up to ~±100: the running max moves often
+    (64, 1, 1, 33, 33, 64, True, 0.0, 1.0),     # many small (batch, head) units
+    (1, 12, 2, 100, 100, 128, True, 10000.0, 1.0),  # 6 query heads per kv head (pairs of heads)
 ]
 
 

@@ -103,11 +103,20 @@ int hip_status(hipError_t e, const char* what) {
 // (caller holds g_mu).  A table built earlier on the same stream for the same
 // first position, D and base that covers npos positions is reused (its values
 // are the same; stream order puts its build before this call's kernels);
-// otherwise the table is rebuilt on `stream`.
+// otherwise the table is rebuilt on `stream`.  While `stream` is being
+// captured into a graph the build is always recorded (a replay must not
+// depend on what the buffer holds then) and the table is not marked as built
+// (the recorded build has not run yet).
 int rope_table(DevBuffers* db, int pos0, int npos, int D, float base, hipStream_t stream,
                const double2** tab, const char* fn) {
-  if (db->tab_ok && db->tab_stream == stream && db->tab_pos0 == pos0 && db->tab_D == D &&
-      db->tab_base == (double)base && db->tab_npos >= npos) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+    (void)hipGetLastError();  // not left for the launch checks that follow
+    cap = hipStreamCaptureStatusNone;
+  }
+  const bool capturing = cap != hipStreamCaptureStatusNone;
+  if (!capturing && db->tab_ok && db->tab_stream == stream && db->tab_pos0 == pos0 &&
+      db->tab_D == D && db->tab_base == (double)base && db->tab_npos >= npos) {
     *tab = static_cast<const double2*>(db->rope_tab);
     return ATTN_OK;
   }
@@ -118,7 +127,7 @@ int rope_table(DevBuffers* db, int pos0, int npos, int D, float base, hipStream_
   hipError_t e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), pos0, npos, D,
                                           (double)base, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: rope table launch: %s", fn, hipGetErrorString(e));
-  db->tab_ok = true;
+  db->tab_ok = !capturing;
   db->tab_pos0 = pos0;
   db->tab_npos = npos;
   db->tab_D = D;

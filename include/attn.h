@@ -31,6 +31,11 @@
  *    needs positions, a head dim or a base that the table does not hold, or
  *    runs on another stream than the one that built it; otherwise it is
  *    reused (the same values, ordered before the call by its stream).
+ *  - HIP graph capture: a call can be captured once the library-owned buffers
+ *    it uses are large enough (an earlier call of the same or a larger shape;
+ *    or pass the workspaces explicitly), since capture cannot allocate.  A
+ *    captured call records its RoPE table build; the library's buffers are
+ *    shared, so replays must be ordered with other calls that use them.
  */
 #ifndef EXACT_ATTN_H
 #define EXACT_ATTN_H

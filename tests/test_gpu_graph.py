@@ -1,0 +1,87 @@
+"""Library calls captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
+
+A decode step (caller-owned workspace) and a forward with RoPE (after one
+eager call of the same shape, so that the library's table and key-staging
+buffers exist and nothing is allocated during capture) are captured once and
+replayed with new input contents, with eager work and synchronisation between
+the replays; every replay must give the eager call's bits.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_28_amd as xa
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _bits_equal(a, b):
+    return torch.equal(a.view(torch.int16), b.view(torch.int16)) if a.dtype != torch.float32 \
+        else torch.equal(a, b)
+
+
+def test_decode_step_in_a_graph():
+    say("case graph decode")
+    cfg = W.Decode("graph", 4, 16, 4, 128, 4096, 100, 4096, 77)
+    qn, kcn, vcn, sln = W.decode_inputs(cfg)
+    q, kc, vc = W.to_device(qn), W.to_device(kcn), W.to_device(vcn)
+    sl = torch.from_numpy(sln).cuda()
+    ns = 8
+    ws = torch.empty(xa.attn_decode_workspace_bytes(cfg.B, cfg.Hq, cfg.D, ns), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.B, cfg.Hq), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up outside the capture
+        xa.attn_decode_splitkv(q, kc, vc, sl, ns, scale=cfg.scale, o=o, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        xa.attn_decode_splitkv(q, kc, vc, sl, ns, scale=cfg.scale, o=o, lse=lse, workspace=ws)
+    rng = np.random.default_rng(5)
+    for rep in range(4):
+        q.copy_(W.to_device(W.f32_to_bf16_bits(
+            rng.standard_normal(tuple(q.shape), dtype=np.float32))))
+        # new lengths within the filled rows (rows past the original ones hold NaN)
+        sl.copy_(torch.from_numpy((rng.integers(1, sln.astype(np.int64) + 1)).astype(np.int32)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_ref, lse_ref = xa.attn_decode_splitkv(q, kc, vc, sl, ns, scale=cfg.scale)
+        torch.cuda.synchronize()
+        assert _bits_equal(o, o_ref) and torch.equal(lse, lse_ref), rep
+
+
+def test_rope_forward_in_a_graph():
+    say("case graph forward")
+    B, Hq, Hkv, S, D = 2, 8, 2, 300, 64
+    rng = np.random.default_rng(6)
+    q, k, v = (W.to_device(W.f32_to_bf16_bits(rng.standard_normal(s, dtype=np.float32)))
+               for s in ((B, S, Hq, D), (B, S, Hkv, D), (B, S, Hkv, D)))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    xa.attn_fwd(q, k, v, causal=True, rope_base=10000.0, o=o, lse=lse)  # buffers exist now
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        xa.attn_fwd(q, k, v, causal=True, rope_base=10000.0, o=o, lse=lse)
+    for rep in range(4):
+        q.copy_(W.to_device(W.f32_to_bf16_bits(rng.standard_normal((B, S, Hq, D),
+                                                                   dtype=np.float32))))
+        k.copy_(W.to_device(W.f32_to_bf16_bits(rng.standard_normal((B, S, Hkv, D),
+                                                                   dtype=np.float32))))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_ref, lse_ref = xa.attn_fwd(q, k, v, causal=True, rope_base=10000.0)
+        torch.cuda.synchronize()
+        assert _bits_equal(o, o_ref) and torch.equal(lse, lse_ref), rep

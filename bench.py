@@ -81,6 +81,18 @@ def timed(fn, reps, stream):
     return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
 
 
+def host_cpu():
+    """The host CPU's model name (from /proc/cpuinfo), or 'unknown'."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(prefill, dec_inputs, budget_s):
     """The fp64 oracle as it stands, timed on this host on a bounded sample:
     prefill (batch, head) units in rounds of one per thread until two thirds of
@@ -103,7 +115,8 @@ def cpu_baseline(prefill, dec_inputs, budget_s):
     flops = cfg.flops / n_units * done
     out = {"value": flops / t_pre / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
            "sample": f"LFM2 GQA prefill, {done} of {n_units} (batch, head) units "
-                     f"(all 4096 query rows each), {t_pre:.1f} s"}
+                     f"(all 4096 query rows each), {t_pre:.1f} s",
+           "host": host_cpu()}
     qd, kc, vc, sl = dec_inputs
     dcfg = W.C5
     all_units = list(range(dcfg.B * dcfg.Hq))

@@ -15,8 +15,9 @@
 //   dq = R^T dQ~, dk = R^T dK~        (RoPE: rotation by the negated angle)
 //
 // Three kernels, deterministic (no atomics):
-//  * bwd_prep_kernel: D_i in fp32, and lse in log2 units with +inf for a row
-//    without visible keys (so that its P is 0).
+//  * bwd_prep_kernel: -D_i in fp32 (the dK/dV kernel starts its dP
+//    accumulators from it, so the MFMAs produce dP - D), and lse in log2 units
+//    with +inf for a row without visible keys (so that its P is 0).
 //  * bwd_dkdv_kernel: one workgroup per (key tile of 128, batch, kv head).  The
 //    tile's K and V stay in registers (MFMA B operands) while the Q and dO
 //    tiles of every query head of the group stream through LDS; per 64-query
@@ -125,7 +126,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const u16* __restrict__ O,
                                                        const u16* __restrict__ dO,
                                                        const float* __restrict__ lse,
-                                                       float* __restrict__ delta,
+                                                       float* __restrict__ ndelta,
                                                        float* __restrict__ lse2, int B, int Sq,
                                                        int Hq) {
   // 8 lanes per (b, i, h) row of 64 16-bit values, rows in [B, Sq, Hq] order
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const u16* __restrict__ O
     const int i = (int)(bi % Sq);
     const int b = (int)(bi / Sq);
     const long long o = ((long long)b * Hq + h) * Sq + i;
-    delta[o] = acc;
+    ndelta[o] = -acc;
     const float l = lse[o];
     lse2[o] = (l == -INFINITY) ? INFINITY : l * kLog2e;
   }
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const u16* __restrict__ O
 template <typename T, bool CAUSAL, bool ROPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
-    const u16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
+    const u16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ ndelta,
     u16* __restrict__ dK, u16* __restrict__ dV, int Hq, int Hkv, int Sq, int Skv, float scale,
     float scale_log2, const double2* __restrict__ tab, int n_bh) {
   constexpr int D = kD, BQ = 64, BK = 128, NKS = D / 16;
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) u16 Qs1[BQ * D];
   __shared__ __attribute__((aligned(16))) u16 Os1[BQ * D];
   __shared__ __attribute__((aligned(16))) float Ls0[BQ];  // lse (log2), per tile row
-  __shared__ __attribute__((aligned(16))) float Ds0[BQ];  // D_i
+  __shared__ __attribute__((aligned(16))) float Ds0[BQ];  // -D_i
   __shared__ __attribute__((aligned(16))) float Ls1[BQ];
   __shared__ __attribute__((aligned(16))) float Ds1[BQ];
 
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (tid < BQ)
         x = (p < Sq) ? lse2[o] : INFINITY;
       else
-        x = (p < Sq) ? delta[o] : 0.f;
+        x = (p < Sq) ? ndelta[o] : 0.f;
     }
     return x;
   };
@@ -269,12 +270,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // whole tile above the diagonal for this wave: every P is 0
     if (CAUSAL && kw0 > p0 + BQ - 1 + off) return;
 
-    // S = Q K^T and dP = dO V^T: blocks of 32 queries (rows) x 32 keys
+    // S = Q K^T and dP - D = dO V^T - D: blocks of 32 queries (rows) x 32 keys,
+    // the dP accumulators starting from the tile rows' -D_i
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[qb][r] = dp[qb][r] = 0.f;
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&ds[32 * qb + 8 * a + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[qb][4 * a + e] = 0.f;
+          dp[qb][4 * a + e] = d4[e];
+        }
+      }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -309,15 +318,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&ds[32 * qb + 8 * a + 4 * g]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * a + e;
-          // k slot r of query block qb: chunk 2 qb + r / 8, element r mod 8
-          pf[2 * qb + r / 8][r % 8] = (T)s[qb][r];
-          sf[2 * qb + r / 8][r % 8] = (T)(s[qb][r] * (dp[qb][r] - d4[e]));
-        }
+      for (int r = 0; r < 16; ++r) {
+        // k slot r of query block qb: chunk 2 qb + r / 8, element r mod 8
+        pf[2 * qb + r / 8][r % 8] = (T)s[qb][r];
+        sf[2 * qb + r / 8][r % 8] = (T)(s[qb][r] * dp[qb][r]);
       }
 
     // dV^T += dO^T P and dK^T += Q^T dS (rows d, columns keys)
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <typename T, int HPW, bool CAUSAL, bool ROPE>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
-    const u16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
+    const u16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ ndelta,
     u16* __restrict__ dQ, int Hq, int Hkv, int Sq, int Skv, float scale, float scale_log2,
     const double2* __restrict__ tab, int n_qt, int n_bh) {
   constexpr int D = kD, BM = 128, BN = 64, NP = BM / HPW, NKS = D / 16;
@@ -398,7 +402,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   const int qlim = CAUSAL ? min(pos + off, Skv - 1) : Skv - 1;
 
   v8 qf[NKS], of[NKS];
-  float l2 = INFINITY, dl = 0.f;
+  float l2 = INFINITY, ndl = 0.f;
   {
     const long long base = (((long long)b * Sq + (qvalid ? pos : 0)) * Hq + hh) * D + g * 8;
 #pragma unroll
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     if (qvalid) {
       const long long st = ((long long)b * Hq + hh) * Sq + pos;
       l2 = lse2[st];
-      dl = delta[st];
+      ndl = ndelta[st];
     }
   }
 
@@ -484,7 +488,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sf[2 * kb + r / 8][r % 8] = (T)(s[kb][r] * (dp[kb][r] - dl));
+      for (int r = 0; r < 16; ++r) sf[2 * kb + r / 8][r % 8] = (T)(s[kb][r] * (dp[kb][r] + ndl));
     // dQ^T += K^T dS^T (rows d, columns queries)
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
@@ -520,7 +524,7 @@ namespace {
 template <typename T, bool C, bool R>
 hipError_t go_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                   const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
-                  int Skv, float scale, const double2* tab, float* delta, float* lse2,
+                  int Skv, float scale, const double2* tab, float* ndelta, float* lse2,
                   hipStream_t stream) {
   const u16* Q = static_cast<const u16*>(q);
   const u16* Kp = static_cast<const u16*>(k);
@@ -532,7 +536,7 @@ hipError_t go_bwd(const void* q, const void* k, const void* v, const void* o, co
   const long long nprep = (nrows + 31) / 32;
   if (nprep > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   bwd_prep_kernel<T><<<dim3((unsigned)nprep), dim3(256), 0, stream>>>(
-      static_cast<const u16*>(o), dO, lse, delta, lse2, B, Sq, Hq);
+      static_cast<const u16*>(o), dO, lse, ndelta, lse2, B, Sq, Hq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -540,7 +544,7 @@ hipError_t go_bwd(const void* q, const void* k, const void* v, const void* o, co
   const long long nkv = (long long)((Skv + 127) / 128) * n_bh_kv;
   if (nkv > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   bwd_dkdv_kernel<T, C, R><<<dim3((unsigned)nkv), dim3(256), 0, stream>>>(
-      Q, Kp, Vp, dO, lse2, delta, static_cast<u16*>(dk), static_cast<u16*>(dv), Hq, Hkv, Sq, Skv,
+      Q, Kp, Vp, dO, lse2, ndelta, static_cast<u16*>(dk), static_cast<u16*>(dv), Hq, Hkv, Sq, Skv,
       scale, sl2, tab, n_bh_kv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -553,7 +557,7 @@ hipError_t go_bwd(const void* q, const void* k, const void* v, const void* o, co
     const long long nb = (long long)n_qt * n_bh;
     if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     bwd_dq_kernel<T, HPW, C, R><<<dim3((unsigned)nb), dim3(256), 0, stream>>>(
-        Q, Kp, Vp, dO, lse2, delta, static_cast<u16*>(dq), Hq, Hkv, Sq, Skv, scale, sl2, tab,
+        Q, Kp, Vp, dO, lse2, ndelta, static_cast<u16*>(dq), Hq, Hkv, Sq, Skv, scale, sl2, tab,
         n_qt, n_bh);
     return hipGetLastError();
   };
@@ -578,7 +582,7 @@ hipError_t launch_bwd16(const void* q, const void* k, const void* v, const void*
   if (D != kD || (dtype != 1 && dtype != 2)) return hipErrorInvalidValue;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   char* ws = static_cast<char*>(workspace);
-  float* delta = reinterpret_cast<float*>(ws);
+  float* ndelta = reinterpret_cast<float*>(ws);
   float* lse2 = reinterpret_cast<float*>(ws + up((size_t)B * Hq * Sq * sizeof(float)));
   const bool rope = rope_tab != nullptr;
   const void* qin = q;
@@ -598,7 +602,7 @@ hipError_t launch_bwd16(const void* q, const void* k, const void* v, const void*
 #define XATTN_BWD_CASE(TT, C, R)                                                               \
   if ((causal != 0) == C && rope == R)                                                         \
     return go_bwd<TT, C, R>(qin, kin, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, scale, \
-                            rope_tab, delta, lse2, stream);
+                            rope_tab, ndelta, lse2, stream);
   if (dtype == 1) {
     XATTN_BWD_CASE(__bf16, false, false)
     XATTN_BWD_CASE(__bf16, true, false)

@@ -54,7 +54,7 @@ hipError_t launch_rope_rotate(const void* x, void* y, int B, int S, int H, int D
 // Backward (16-bit: dtype 1 bf16, 2 fp16; D = 64): q, k, v, o, dout like the
 // forward's tensors, lse its [B,Hq,Sq] output; dq like q, dk and dv like k.
 // rope_tab: table rows for positions [0, Skv) (null: no RoPE).  workspace:
-// bwd_workspace_bytes bytes (per-row D and log2 lse, then, with RoPE, the
+// bwd_workspace_bytes bytes (per-row -D and log2 lse, then, with RoPE, the
 // rotated Q and K).
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D, bool rope);
 hipError_t launch_bwd16(const void* q, const void* k, const void* v, const void* o,

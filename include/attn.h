@@ -136,7 +136,7 @@ int attn_fwd_masked(const void* q, const void* k, const void* v, const float* ma
 
 /*
  * attn_bwd_workspace_bytes — size of the workspace attn_bwd needs: the per-row
- * D_i and log2 lse ([B, Hq, Sq] fp32 each) and, with rope_base > 0, the rotated
+ * -D_i and log2 lse ([B, Hq, Sq] fp32 each) and, with rope_base > 0, the rotated
  * Q and K (B*Sq*Hq*D and B*Skv*Hkv*D 16-bit values), each part rounded up to 256 bytes.
  * Returns 0 for invalid sizes.
  */

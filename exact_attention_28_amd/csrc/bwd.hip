@@ -455,11 +455,15 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   auto tile = [&](int t, const u16* ks_, const u16* vs_) __attribute__((always_inline)) {
     const int k0 = t * BN;
     // S^T = K Q^T and dP^T = V dO^T: blocks of 32 keys (rows) x 32 queries
+    // (dP^T accumulators start from this lane's query's -D_i: the MFMAs yield dP - D)
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) {
+        s[kb][r] = 0.f;
+        dp[kb][r] = ndl;
+      }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -488,7 +492,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sf[2 * kb + r / 8][r % 8] = (T)(s[kb][r] * (dp[kb][r] + ndl));
+      for (int r = 0; r < 16; ++r) sf[2 * kb + r / 8][r % 8] = (T)(s[kb][r] * dp[kb][r]);
     // dQ^T += K^T dS^T (rows d, columns queries)
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)

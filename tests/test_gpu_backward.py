@@ -153,3 +153,33 @@ def test_bwd_deterministic_and_workspace():
     for x, y in zip(a, b2):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
     assert (guard[:1024] == 7.0).all() and (guard[1024 + B * Sq * Hq * D:] == 7.0).all()
+
+
+def test_bwd_guard_regions():
+    """Every input of the backward sits between NaN guard regions and every
+    output between sentinel regions: a read past an input turns a gradient
+    NaN, a write past an output changes a sentinel."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 190, 64
+    rng = np.random.default_rng(13)
+    q, k, v, do = _inputs(rng, B, Hq, Hkv, S, S, D)
+    G = 1 << 14
+
+    def guarded(t, fill):
+        flat = torch.full((t.numel() + 2 * G,), fill, dtype=t.dtype, device="cuda")
+        flat[G:G + t.numel()] = t.reshape(-1)
+        return flat, flat[G:G + t.numel()].view(t.shape)
+
+    qd, kd, vd, dod = (W.to_device(x) for x in (q, k, v, do))
+    for causal, rope in ((True, 10000.0), (False, 0.0)):
+        o, lse = xa.attn_fwd(qd, kd, vd, causal=causal, rope_base=rope)
+        gq, gk, gv, go, gdo, gl = (guarded(t, float("nan"))[1] for t in (qd, kd, vd, o, dod, lse))
+        outs = [guarded(torch.empty_like(t), 7.0) for t in (qd, kd, vd)]
+        dq, dk, dv = xa.attn_bwd(gq, gk, gv, go, gdo, gl, causal=causal, rope_base=rope,
+                                 dq=outs[0][1], dk=outs[1][1], dv=outs[2][1])
+        torch.cuda.synchronize()
+        ref = oracle.attn_bwd(q, k, v, do, causal=causal, scale=1 / math.sqrt(D),
+                              rope_base=rope, nthreads=NTHREADS)
+        for g, r, n in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+            check_grad(_np(g), r, f"guarded causal={causal} {n}")
+        for flat, view in outs:
+            assert (flat[:G] == 7.0).all() and (flat[G + view.numel():] == 7.0).all()

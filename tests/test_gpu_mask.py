@@ -183,3 +183,26 @@ def test_lfm2_workload_with_mask_sampled():
     og = o[:, rows].transpose(0, 2, 1, 3).reshape(cfg.B * cfg.Hq, len(rows), cfg.D)
     lg = lse[:, :, rows].reshape(cfg.B * cfg.Hq, len(rows))
     check_bf16(og, lg, o_ref, lse_ref, f"{cfg.name} masked")
+
+
+def test_mask_between_nan_guards():
+    """The mask sits between NaN guard regions (16-byte aligned, 100 keys: the
+    staged path, whose loads of the last row's chunks reach the range end);
+    any value read past the mask's valid elements that reached a score would
+    turn the output NaN."""
+    B, Hq, Hkv, Sq, Skv, D = 1, 8, 2, 70, 100, 64
+    rng = np.random.default_rng(12)
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, Sq, Hq, D), dtype=np.float32))
+    k = W.f32_to_bf16_bits(rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32))
+    v = W.f32_to_bf16_bits(rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32))
+    mask = _mask(rng, (Sq, Skv))
+    G = 1 << 14
+    flat = torch.full((Sq * Skv + 2 * G,), float("nan"), dtype=torch.float32, device="cuda")
+    flat[G:G + Sq * Skv] = torch.from_numpy(mask).cuda().reshape(-1)
+    for causal in (True, False):
+        o, lse = xa.attn_fwd_masked(W.to_device(q), W.to_device(k), W.to_device(v),
+                                    flat[G:G + Sq * Skv].view(Sq, Skv), causal=causal,
+                                    scale=0.125)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = _oracle(q, k, v, mask, causal, 0.125, 0.0, B, Hq, Sq, Skv)
+        check_bf16(_np(o), _np(lse), o_ref, lse_ref, f"mask guarded causal={causal}")

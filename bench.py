@@ -184,6 +184,24 @@ def profile_decode(reps):
     log(f"profile-decode done (algorithmic KV bytes per call {kv_bytes})")
 
 
+def profile_backward(reps):
+    """For counter runs: `reps` calls of attn_bwd on the LFM2 prefill workload
+    (causal, RoPE), after the forward that gives its O and LSE."""
+    pc = W.C4
+    q_np, k_np, v_np = W.prefill_inputs(pc)
+    q, k, v = W.to_device(q_np), W.to_device(k_np), W.to_device(v_np)
+    dout = W.to_device(W.f32_to_bf16_bits(
+        np.random.default_rng(pc.seed + 7).standard_normal(q_np.shape, dtype=np.float32)))
+    o, lse = xa.attn_fwd(q, k, v, causal=True, scale=pc.scale, rope_base=pc.rope_base)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        xa.attn_bwd(q, k, v, o, dout, lse, causal=True, scale=pc.scale, rope_base=pc.rope_base,
+                    dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    log("profile-backward done")
+
+
 def counters_summary(csv_path, match, out_path, title, cmds):
     """Per-dispatch means of every counter in a rocprofv3 counter_collection
     CSV for the kernels whose name contains `match`, with the calibration
@@ -280,6 +298,8 @@ def main():
                     help="command line recorded in the traffic summary (repeatable)")
     ap.add_argument("--profile-decode", type=int, default=0, metavar="REPS",
                     help="only run the split-KV decode REPS times, then a calibration copy")
+    ap.add_argument("--profile-backward", type=int, default=0, metavar="REPS",
+                    help="only run the LFM2 prefill backward REPS times")
     ap.add_argument("--counters-summary", nargs=4, metavar=("CSV", "MATCH", "OUT", "TITLE"),
                     help="write per-dispatch counter means of kernels matching MATCH")
     args = ap.parse_args()
@@ -300,6 +320,9 @@ def main():
         return
     if args.profile_decode:
         profile_decode(args.profile_decode)
+        return
+    if args.profile_backward:
+        profile_backward(args.profile_backward)
         return
     stream = torch.cuda.current_stream()
 

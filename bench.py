@@ -81,6 +81,23 @@ def timed(fn, reps, stream):
     return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
 
 
+def settle(fn, seconds):
+    """Run fn back to back, untimed, for about `seconds`; returns the call count.
+
+    Under a sustained load the GPU moves its clocks over tens to hundreds of
+    milliseconds (up at first, down when a heavier kernel starts), so each
+    measurement is preceded by its own workload run long enough that the
+    timed calls see the clocks that workload holds when it runs continuously."""
+    t_end = time.perf_counter() + seconds
+    n = 0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+        n += 8
+    return n
+
+
 def host_cpu():
     """The host CPU's model name (from /proc/cpuinfo), or 'unknown'."""
     try:
@@ -288,6 +305,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle", type=float, default=0.5, metavar="SECONDS",
+                    help="untimed steps for this long before the warmup steps (clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=24.0)
     ap.add_argument("--profile-kernel", type=int, default=0, metavar="REPS",
@@ -349,6 +368,11 @@ def main():
         xa.attn_decode_splitkv(dq, kc, vc, sl, ns, scale=dc.scale, o=do, lse=dlse,
                                workspace=ws[ns])
 
+    # ---- settle (a fresh process's first 10-call block of the prefill runs
+    # ~25 % slower than its steady state): untimed steps for `--settle` seconds
+    log("settle")
+    n_settle = settle(lambda: (prefill(), decode(dc.splits[0])), args.settle)
+
     # ---- warmup, and the split count for the decode half (outside the timed region)
     log("warmup")
     for _ in range(max(args.warmup, 1)):
@@ -405,8 +429,7 @@ def main():
     def backward():
         xa.attn_bwd(q, k, v, o, dout, lse, causal=True, scale=pc.scale, rope_base=pc.rope_base,
                     dq=dq, dk=dk, dv=dv, workspace=bwd_ws)
-    for _ in range(3):
-        backward()
+    settle(backward, args.settle / 2)
     bwd_ms = timed(backward, max(args.steps // 2, 10), stream)
     bwd_tflops = 2.5 * pc.flops / (bwd_ms * 1e-3) / 1e12
 
@@ -428,8 +451,7 @@ def main():
                                     scale=pc.scale, rope_base=pc.rope_base, o=och[i],
                                     want_lse=False)
             lens.add_(CH)
-    for _ in range(3):
-        chunked()
+    settle(chunked, args.settle / 2)
     ch_ms = timed(chunked, max(args.steps // 2, 10), stream)
     ch_tflops = pc.flops / (ch_ms * 1e-3) / 1e12
 
@@ -444,8 +466,7 @@ def main():
     def masked():
         xa.attn_fwd_masked(q, k, v, bias, causal=True, scale=pc.scale, rope_base=pc.rope_base,
                            o=o, lse=lse)
-    for _ in range(3):
-        masked()
+    settle(masked, args.settle / 2)
     mk_ms = timed(masked, max(args.steps // 2, 10), stream)
     mk_tflops = pc.flops / (mk_ms * 1e-3) / 1e12
 
@@ -470,6 +491,8 @@ def main():
             "decode": {"B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv, "D": dc.D, "Smax": dc.Smax,
                        "sum_lengths": int(sl_np.sum()), "num_splits": best_ns, "seed": dc.seed},
             "parallelism": "single GPU",
+            "settle": {"seconds": args.settle, "untimed_steps": n_settle,
+                       "seconds_before_backward_chunked_masked": args.settle / 2},
         },
         "prefill": {"ms": round(pre_ms, 4), "tflops": round(pre_tflops, 2),
                     "frac_of_mfma_peak": round(pre_tflops / PEAK_BF16_TFLOPS, 4)},

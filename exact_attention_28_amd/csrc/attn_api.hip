@@ -213,6 +213,10 @@ int fwd(const char* fn, const void* q, const void* k, const void* v, void* o, fl
     return fwd_padded(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, rope_base, dtype,
                       mask, stream);
 
+  // RoPE: the fp32 kernel rotates queries and keys as it loads them; the
+  // 16-bit kernel rotates its query fragments in its prologue, and the keys,
+  // which every query tile reads, are rotated once by a pass into a
+  // library-owned copy
   const double2* tab = nullptr;
   const void* kin = k;
   if (rope) {
@@ -221,11 +225,11 @@ int fwd(const char* fn, const void* q, const void* k, const void* v, void* o, fl
     DevBuffers* db = buffers(&st);
     if (!db) return st;
     if ((st = rope_table(db, 0, Skv, D, rope_base, stream, &tab, fn)) != ATTN_OK) return st;
-    hipError_t e;
     if (dtype != ATTN_F32) {
       const size_t kb = (size_t)B * Skv * Hkv * D * 2;
       if ((st = grow(&db->kstage, &db->kstage_bytes, kb, "rotated K")) != ATTN_OK) return st;
-      e = xattn::launch_rope_rotate(k, db->kstage, B, Skv, Hkv, D, tab, dtype, stream);
+      hipError_t e = xattn::launch_rope_rotate_qk(nullptr, nullptr, B, Sq, Hq, k, db->kstage, Skv,
+                                                  Hkv, D, tab, dtype, stream);
       if (e != hipSuccess) return hip_status(e, "attn_fwd: K rotation launch");
       kin = db->kstage;
     }

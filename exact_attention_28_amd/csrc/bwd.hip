@@ -594,11 +594,9 @@ hipError_t launch_bwd16(const void* q, const void* k, const void* v, const void*
   if (rope) {
     char* qs = ws + 2 * up((size_t)B * Hq * Sq * sizeof(float));
     char* ks = qs + up((size_t)B * Sq * Hq * D * 2);
-    // queries at positions Skv - Sq + i: table rows from Skv - Sq on
-    hipError_t e = launch_rope_rotate(q, qs, B, Sq, Hq, D, rope_tab + (size_t)(Skv - Sq) * (D / 2),
-                                      dtype, stream);
-    if (e != hipSuccess) return e;
-    e = launch_rope_rotate(k, ks, B, Skv, Hkv, D, rope_tab, dtype, stream);
+    // one pass: queries at positions Skv - Sq + i, keys at j
+    hipError_t e =
+        launch_rope_rotate_qk(q, qs, B, Sq, Hq, k, ks, Skv, Hkv, D, rope_tab, dtype, stream);
     if (e != hipSuccess) return e;
     qin = qs;
     kin = ks;

@@ -154,29 +154,6 @@ __attribute__((amdgpu_waves_per_eu(MASK == 3 && HPW >= 4 ? 3 : 1))) void fwd16_k
     qvalid[qb] = pos[qb] < Sq;
   }
 
-  // ---- query fragments: lane holds q[pos, hh, 16ks + 8g .. +7] for every ks
-  v8 qf[NQB][NKS];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const u16* qp =
-        Q + (((long long)b * Sq + (qvalid[qb] ? pos[qb] : 0)) * Hq + hh[qb]) * D + g * 8;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 wv = {0u, 0u, 0u, 0u};
-      if (qvalid[qb]) wv = *reinterpret_cast<const u32x4*>(qp + ks * 16);
-      if (ROPE && qvalid[qb]) {
-        const double2* tp = tab + (long long)(off + pos[qb]) * (D / 2) + ks * 8 + g * 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          double r0, r1;
-          rotate_pair((double)F::lo(wv[e]), (double)F::hi(wv[e]), tp[e], r0, r1);
-          wv[e] = F::from_f64(r0) | (F::from_f64(r1) << 16);
-        }
-      }
-      qf[qb][ks] = __builtin_bit_cast(v8, wv);
-    }
-  }
-
   // with a mask, the scores are scaled (and the mask added) right after the
   // contraction, so the softmax below only converts to base 2
   const float sl = MASK ? kLog2e : scale_log2;
@@ -313,11 +290,67 @@ __attribute__((amdgpu_waves_per_eu(MASK == 3 && HPW >= 4 ? 3 : 1))) void fwd16_k
     l_run[qb] = 0.f;
   }
 
-  if (ntiles > 0) {
-    dma(0, Ks0, Vs0);
-    if constexpr (MASK == 2) dma_rows<8>(rm, reinterpret_cast<u16*>(Mw), moff, 0u);
-    if constexpr (MASK == 3) dma_rows<NI>(rm, reinterpret_cast<u16*>(Mx0 + w * NI * 256), moff, 0u);
+  // ---- query fragments: lane holds q[pos, hh, 16ks + 8g .. +7] for every ks.
+  // Columns past Sq read row 0 (and its table row) and are zeroed afterwards:
+  // with no per-lane branch every load of the prologue (fragments, table
+  // entries, the first tile) is in flight at once, and the rotation waits for
+  // its own operands only, while the tile's direct loads land.
+  v8 qf[NQB][NKS];
+  {
+    u32x4 qw[NQB][NKS];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const u16* qp =
+          Q + (((long long)b * Sq + (qvalid[qb] ? pos[qb] : 0)) * Hq + hh[qb]) * D + g * 8;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qw[qb][ks] = *reinterpret_cast<const u32x4*>(qp + ks * 16);
+    }
+    double2 cs[NQB][NKS][4];
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const double2* tp =
+            tab + (long long)(off + (qvalid[qb] ? pos[qb] : 0)) * (D / 2) + g * 4;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cs[qb][ks][e] = tp[ks * 8 + e];
+      }
+    }
+    if (ntiles > 0) {
+      dma(0, Ks0, Vs0);
+      if constexpr (MASK == 2) dma_rows<8>(rm, reinterpret_cast<u16*>(Mw), moff, 0u);
+      if constexpr (MASK == 3)
+        dma_rows<NI>(rm, reinterpret_cast<u16*>(Mx0 + w * NI * 256), moff, 0u);
+    }
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            double r0, r1;
+            rotate_pair((double)F::lo(qw[qb][ks][e]), (double)F::hi(qw[qb][ks][e]),
+                        cs[qb][ks][e], r0, r1);
+            qw[qb][ks][e] = F::from_f64(r0) | (F::from_f64(r1) << 16);
+          }
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        u32x4 wv = qw[qb][ks];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[e] = qvalid[qb] ? wv[e] : 0u;
+        // an empty register constraint keeps the fragment (and so its loads)
+        // ahead of the barrier below, which the compiler would otherwise let
+        // read-only loads sink past
+        asm volatile("" : "+v"(wv));
+        qf[qb][ks] = __builtin_bit_cast(v8, wv);
+      }
   }
+
   // everything the prologue loaded (query fragments, first tile) has landed
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();

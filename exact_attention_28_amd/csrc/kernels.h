@@ -50,6 +50,13 @@ hipError_t launch_rope_table(double2* tab, int pos0, int npos, int D, double bas
 // token t uses table row t.
 hipError_t launch_rope_rotate(const void* x, void* y, int B, int S, int H, int D,
                               const double2* tab, int dtype, hipStream_t stream);
+// Rotate an attention call's q [B,Sq,Hq,D] into qo (q non-null) and k
+// [B,Skv,Hkv,D] into ko (k non-null) in one launch, dtype 1 bf16 / 2 fp16,
+// D % 8 == 0, B <= 65535, Sq <= Skv when q is given: key row t uses table row
+// t, query row t table row Skv - Sq + t.
+hipError_t launch_rope_rotate_qk(const void* q, void* qo, int B, int Sq, int Hq, const void* k,
+                                 void* ko, int Skv, int Hkv, int D, const double2* tab, int dtype,
+                                 hipStream_t stream);
 
 // Backward (16-bit: dtype 1 bf16, 2 fp16; D = 64): q, k, v, o, dout like the
 // forward's tensors, lse its [B,Hq,Sq] output; dq like q, dk and dv like k.

@@ -92,6 +92,64 @@ __global__ void rope_rotate_pair(const void* xv, void* yv,
   }
 }
 
+// Queries and keys of an attention call in one launch (16-bit formats,
+// D % 8 == 0): block (t, b) rotates, when q is given, query row t of batch b
+// (Hq heads) at position Skv - Sq + t (bottom-right alignment) and, when k is
+// given, key row t (Hkv heads) at position t.  A row is D / 8 chunks of 16
+// bytes, one per thread; the token index comes from the grid, so no thread
+// divides a 64-bit index.
+template <typename T>
+__global__ void rope_rotate_qk16(const u16* __restrict__ q, u16* __restrict__ qo, int Sq, int Hq,
+                                 const u16* __restrict__ k, u16* __restrict__ ko, int Skv,
+                                 int Hkv, int D, const double2* __restrict__ tab) {
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int cpr = D / 8, half = D / 2;
+  auto rotate_row = [&](const u16* x, u16* y, int nchunks, const double2* trow) {
+    for (int c = threadIdx.x; c < nchunks; c += blockDim.x) {
+      const int part = c % cpr;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(x + (long long)c * 8);
+      u32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        double r0, r1;
+        rotate_pair((double)Fmt16<T>::lo(w[e]), (double)Fmt16<T>::hi(w[e]), trow[part * 4 + e],
+                    r0, r1);
+        r[e] = Fmt16<T>::from_f64(r0) | (Fmt16<T>::from_f64(r1) << 16);
+      }
+      *reinterpret_cast<u32x4*>(y + (long long)c * 8) = r;
+    }
+  };
+  if (q != nullptr && t < Sq) {
+    const long long row = ((long long)b * Sq + t) * Hq * D;
+    rotate_row(q + row, qo + row, Hq * cpr, tab + (long long)(Skv - Sq + t) * half);
+  }
+  if (k != nullptr && t < Skv) {
+    const long long row = ((long long)b * Skv + t) * Hkv * D;
+    rotate_row(k + row, ko + row, Hkv * cpr, tab + (long long)t * half);
+  }
+}
+
+hipError_t launch_rope_rotate_qk(const void* q, void* qo, int B, int Sq, int Hq, const void* k,
+                                 void* ko, int Skv, int Hkv, int D, const double2* tab, int dtype,
+                                 hipStream_t stream) {
+  if ((dtype != 1 && dtype != 2) || D % 8 != 0 || B > 65535 || (q && Sq > Skv))
+    return hipErrorInvalidValue;
+  const int rows = max(q ? Sq : 0, k ? Skv : 0);
+  const int most = max(q ? Hq : 0, k ? Hkv : 0) * (D / 8);  // chunks of the widest row
+  if (rows == 0) return hipSuccess;
+  const int threads = min(256, (most + 63) / 64 * 64);
+  const dim3 grid((unsigned)rows, (unsigned)B);
+  if (dtype == 1)
+    rope_rotate_qk16<__bf16><<<grid, dim3(threads), 0, stream>>>(
+        static_cast<const u16*>(q), static_cast<u16*>(qo), Sq, Hq, static_cast<const u16*>(k),
+        static_cast<u16*>(ko), Skv, Hkv, D, tab);
+  else
+    rope_rotate_qk16<_Float16><<<grid, dim3(threads), 0, stream>>>(
+        static_cast<const u16*>(q), static_cast<u16*>(qo), Sq, Hq, static_cast<const u16*>(k),
+        static_cast<u16*>(ko), Skv, Hkv, D, tab);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_rotate(const void* x, void* y, int B, int S, int H, int D,
                               const double2* tab, int dtype, hipStream_t stream) {
   const long long rows = (long long)B * S * H;

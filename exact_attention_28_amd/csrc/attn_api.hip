@@ -309,7 +309,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   // 32-bit buffer offsets within one batch; grid sizes
   if ((long long)Sq * Hq * D * 2 >= 0x7fffffffLL || (long long)Skv * Hkv * D * 2 >= 0x7fffffffLL)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: one batch's Q or K exceeds 2 GiB");
-  if ((long long)B * Hq * ((Sq + 31) / 32) > 0x7fffffffLL)
+  if ((long long)B * Hq * ((Sq + 31) / 32) > 0x7fffffffLL || (rope && B > 65535))
     return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: grid too large");
 
   std::lock_guard<std::mutex> lock(g_mu);

@@ -170,6 +170,7 @@ def _bwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAK
     (dict(dtype=2, D=128), xa.ATTN_ERR_UNSUPPORTED),
     (dict(D=128), xa.ATTN_ERR_UNSUPPORTED),
     (dict(Sq=16, Skv=8, rope=10000.0), xa.ATTN_ERR_UNSUPPORTED),
+    (dict(B=65536, Sq=1, Skv=1, Hq=2, Hkv=2, rope=10000.0), xa.ATTN_ERR_UNSUPPORTED),
 ])
 def test_bwd_validation(lib, kw, code):
     assert _bwd(lib, **kw) == code

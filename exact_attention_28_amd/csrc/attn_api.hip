@@ -14,9 +14,12 @@
 #include <cstdint>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "attn.h"
 #include "kernels.h"
@@ -93,6 +96,34 @@ DevBuffers* buffers(int* status) {
 }
 
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.f; }
+
+// With ATTN_DEBUG=1 in the environment, lengths that live in device memory
+// (decode seqlens, cache_lens) are copied to the host and checked against
+// [lo, hi] before the launch.  The copy is synchronous on the call's stream,
+// so the call first waits for the work already queued there; during graph
+// capture, where such a copy cannot run, the check is skipped.
+int debug_check_lens(const char* fn, const char* what, const int* lens, int B, int lo, int hi,
+                     hipStream_t stream) {
+  const char* env = std::getenv("ATTN_DEBUG");
+  if (env == nullptr || std::strcmp(env, "1") != 0) return ATTN_OK;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    cap = hipStreamCaptureStatusNone;
+  }
+  if (cap != hipStreamCaptureStatusNone) return ATTN_OK;
+  std::vector<int> h((size_t)B);
+  hipError_t e = hipMemcpyAsync(h.data(), lens, (size_t)B * sizeof(int), hipMemcpyDeviceToHost,
+                                stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess)
+    return fail(ATTN_ERR_HIP, "%s: ATTN_DEBUG copy of %s: %s", fn, what, hipGetErrorString(e));
+  for (int b = 0; b < B; ++b)
+    if (h[(size_t)b] < lo || h[(size_t)b] > hi)
+      return fail(ATTN_ERR_INVALID, "%s: %s[%d] = %d outside [%d, %d] (ATTN_DEBUG)", fn, what, b,
+                  h[(size_t)b], lo, hi);
+  return ATTN_OK;
+}
 
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
@@ -358,6 +389,9 @@ int attn_decode_splitkv(const void* q, const void* kcache, const void* vcache,
     return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_splitkv: D=%d (built: 64, 128)", D);
   if (B > 65535 || Hq > 65535 || (long long)B * Hq > 0x7fffffffLL)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_splitkv: grid too large");
+  if (int st = debug_check_lens("attn_decode_splitkv", "seqlens", seqlens, B, 0, max_seqlen,
+                                stream))
+    return st;
 
   void* ws = workspace;
   if (ws == nullptr) {
@@ -406,6 +440,10 @@ int attn_prefill_kvcache(const void* q, const void* k_new, const void* v_new, vo
     return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_kvcache: one batch's cache exceeds 2 GiB");
   if ((long long)B * Hq * ((Sq + 15) / 16) > 0x7fffffffLL || B > 65535 || Hq > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_kvcache: grid too large");
+
+  if (int st = debug_check_lens("attn_prefill_kvcache", "cache_lens", cache_lens, B, 0,
+                                max_seqlen - Sq, stream))
+    return st;
 
   const double2* tab = nullptr;
   if (rope) {

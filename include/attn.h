@@ -205,7 +205,11 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
  *           never read
  *   seqlens [B] int32 in device memory, 0 <= seqlens[b] <= max_seqlen
  *           (a precondition: it is not checked on the host because the values
- *           live on the device; larger values are clamped to max_seqlen)
+ *           live on the device; larger values are clamped to max_seqlen).
+ *           With ATTN_DEBUG=1 in the environment the call copies seqlens to
+ *           the host first (synchronously on `stream`, so it waits for the
+ *           work queued there; skipped during graph capture) and returns
+ *           ATTN_ERR_INVALID, launching nothing, if a value is out of range.
  *   o       [B, Hq, D] bf16 (output);  lse [B, Hq] fp32 (output, may be NULL)
  *   B, Hq, Hkv >= 1; Hq % Hkv == 0; D in {64, 128}; 1 <= num_splits <= 64;
  *   max_seqlen >= 1; scale finite and > 0
@@ -242,7 +246,8 @@ int attn_decode_splitkv(const void* q, const void* kcache, const void* vcache,
  *          [L_b, L_b + Sq) written, later rows neither read nor written)
  *   cache_lens [B] int32 in device memory, 0 <= cache_lens[b] <= max_seqlen - Sq
  *          (a precondition, as for attn_decode_splitkv: values outside are
- *          clamped into that range)
+ *          clamped into that range; checked on the host, as there, with
+ *          ATTN_DEBUG=1)
  *   o [B, Sq, Hq, D] bf16 (output);  lse [B, Hq, Sq] fp32 (output, may be NULL)
  *   B, Hq, Hkv, Sq >= 1; Hq % Hkv == 0; D in {64, 128}; 1 <= Sq <= max_seqlen;
  *   causal 0 or 1; scale finite and > 0; rope_base > 0 enables RoPE (D even)

@@ -34,6 +34,7 @@ import workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 METRIC = "attention fwd TFLOP/s + decode KV GB/s, as % of MI355X MFMA/HBM peak"
 KERNEL_SOURCES = ("fwd16.hip", "common.h", "lds.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd16_lfm2_gqa_prefill_s4096_traffic.txt")
@@ -79,6 +80,21 @@ def timed(fn, reps, stream):
         ends[i].record(stream)
     torch.cuda.synchronize()
     return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+
+
+def timed_queued(fn, reps, stream):
+    """Mean GPU time (ms) per call of fn over reps back-to-back calls.  A spin
+    kernel (about 1.5 ms) runs first, so the host has enqueued the calls
+    before the first one starts: for calls shorter than their host-side
+    launch cost, the events then bracket GPU time, not launch overhead."""
+    torch.cuda._sleep(3_000_000)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def settle(fn, seconds):
@@ -154,22 +170,24 @@ def cpu_baseline(prefill, dec_inputs, budget_s):
 COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
 
 
-def profile_kernel(reps):
+def profile_kernel(reps, workload):
     """For counter runs: `reps` launches of the prefill kernel alone (Q and K
-    rotated beforehand) on the LFM2 prefill workload, then `reps` launches of a
-    plain elementwise copy of COPY_BYTES (dst = src + 0) for calibration."""
-    pc = W.C4
+    rotated beforehand when the workload has RoPE) on the named prefill
+    workload (default the LFM2 prefill), then `reps` launches of a plain
+    elementwise copy of COPY_BYTES (dst = src + 0) for calibration."""
+    pc = {c.name: c for c in W.PREFILL}[workload]
     q_np, k_np, v_np = W.prefill_inputs(pc)
     q, k, v = W.to_device(q_np), W.to_device(k_np), W.to_device(v_np)
-    xa.rope_apply(q, 0, pc.rope_base)
-    xa.rope_apply(k, 0, pc.rope_base)
+    if pc.rope_base > 0:
+        xa.rope_apply(q, 0, pc.rope_base)
+        xa.rope_apply(k, 0, pc.rope_base)
     o = torch.empty_like(q)
     lse = torch.empty((pc.B, pc.Hq, pc.Sq), dtype=torch.float32, device="cuda")
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(reps):
-        xa.attn_fwd(q, k, v, causal=True, scale=pc.scale, o=o, lse=lse)
+        xa.attn_fwd(q, k, v, causal=pc.causal, scale=pc.scale, o=o, lse=lse)
     torch.cuda.synchronize()
     for _ in range(reps):
         torch.add(src, 0.0, out=dst)
@@ -309,6 +327,9 @@ def main():
                     help="untimed steps for this long before the warmup steps (clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=24.0)
+    ap.add_argument("--profile-workload", default=W.C4.name,
+                    choices=[c.name for c in W.PREFILL],
+                    help="prefill workload of --profile-kernel")
     ap.add_argument("--profile-kernel", type=int, default=0, metavar="REPS",
                     help="only launch the prefill kernel REPS times, then a calibration copy")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -335,7 +356,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     if args.profile_kernel:
-        profile_kernel(args.profile_kernel)
+        profile_kernel(args.profile_kernel, args.profile_workload)
         return
     if args.profile_decode:
         profile_decode(args.profile_decode)
@@ -470,6 +491,28 @@ def main():
     mk_ms = timed(masked, max(args.steps // 2, 10), stream)
     mk_tflops = pc.flops / (mk_ms * 1e-3) / 1e12
 
+    # ---- the other prefill workloads (the parity cases' shapes), one call each
+    # (GPU time: the host's launch cost is kept out), for context: a single
+    # fp32 head (fp32 VALU path), MHA at 1024 tokens without and with the
+    # causal mask, the Whisper-encoder shape
+    others = {}
+    for c in (W.C1, W.C2N, W.C2C, W.C3):
+        qo_, ko_, vo_ = (W.to_device(x) for x in W.prefill_inputs(c))
+        oo_ = torch.empty_like(qo_)
+        lo_ = torch.empty((c.B, c.Hq, c.Sq), dtype=torch.float32, device="cuda")
+
+        def call(c=c, qo_=qo_, ko_=ko_, vo_=vo_, oo_=oo_, lo_=lo_):
+            xa.attn_fwd(qo_, ko_, vo_, causal=c.causal, scale=c.scale, o=oo_, lse=lo_)
+        settle(call, args.settle / 5)
+        c_ms = timed_queued(call, max(args.steps, 20), stream)
+        c_tf = c.flops / (c_ms * 1e-3) / 1e12
+        others[c.name] = {"shape": f"B{c.B} Hq{c.Hq} Hkv{c.Hkv} S{c.Sq} D{c.D} {c.dtype}"
+                                   f"{' causal' if c.causal else ''}",
+                          "ms": round(c_ms, 4), "tflops": round(c_tf, 3),
+                          "frac_of_peak": round(c_tf / (PEAK_F32_TFLOPS if c.dtype == "f32"
+                                                        else PEAK_BF16_TFLOPS), 4)}
+        del qo_, ko_, vo_, oo_, lo_
+
     result = {
         "metric": METRIC,
         "value": round(pre_tflops, 2),
@@ -516,6 +559,7 @@ def main():
                                        "additive mask (distance bias, 2048-key window), causal",
                            "ms": round(mk_ms, 4), "tflops": round(mk_tflops, 2),
                            "frac_of_mfma_peak": round(mk_tflops / PEAK_BF16_TFLOPS, 4)},
+        "other_prefill_workloads": others,
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1),
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                             "frac": round(dec_gbps / PEAK_HBM_GBPS, 4)},

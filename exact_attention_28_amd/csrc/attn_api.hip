@@ -61,6 +61,8 @@ struct DevBuffers {
   size_t bwd_ws_bytes = 0;
   void* pad_ws = nullptr;
   size_t pad_ws_bytes = 0;
+  void* split_ws = nullptr;  // key-split partials of under-filled forward launches
+  size_t split_ws_bytes = 0;
 };
 
 std::mutex g_mu;
@@ -123,6 +125,37 @@ int debug_check_lens(const char* fn, const char* what, const int* lens, int B, i
       return fail(ATTN_ERR_INVALID, "%s: %s[%d] = %d outside [%d, %d] (ATTN_DEBUG)", fn, what, b,
                   h[(size_t)b], lo, hi);
   return ATTN_OK;
+}
+
+// Key splits for a 16-bit forward launch (unmasked; kv_rows = keys, or the
+// cache capacity) and, when there are any, the library-owned partial buffer.
+// The caller holds g_mu.
+int plan_splits_locked(DevBuffers* db, int B, int Hq, int Hkv, int Sq, int kv_rows, int D,
+                       bool masked, xattn::KeySplit* ks) {
+  *ks = xattn::KeySplit();
+  if (masked) return ATTN_OK;
+  const int n = xattn::fwd16_key_splits(B, Hq, Hkv, Sq, kv_rows, D);
+  if (n <= 1) return ATTN_OK;
+  const size_t rows = (size_t)B * Sq * Hq;
+  const size_t obytes = (rows * n * D * 4 + 255) & ~(size_t)255;
+  int st = grow(&db->split_ws, &db->split_ws_bytes, xattn::fwd16_split_ws_bytes(B, Hq, Sq, D, n),
+                "key-split partials");
+  if (st != ATTN_OK) return st;
+  ks->n = n;
+  ks->o = static_cast<float*>(db->split_ws);
+  ks->l = reinterpret_cast<float*>(static_cast<char*>(db->split_ws) + obytes);
+  return ATTN_OK;
+}
+
+int plan_splits(int B, int Hq, int Hkv, int Sq, int kv_rows, int D, bool masked,
+                xattn::KeySplit* ks) {
+  *ks = xattn::KeySplit();
+  if (masked || xattn::fwd16_key_splits(B, Hq, Hkv, Sq, kv_rows, D) <= 1) return ATTN_OK;
+  std::lock_guard<std::mutex> lock(g_mu);
+  int st;
+  DevBuffers* db = buffers(&st);
+  if (!db) return st;
+  return plan_splits_locked(db, B, Hq, Hkv, Sq, kv_rows, D, masked, ks);
 }
 
 int hip_status(hipError_t e, const char* what) {
@@ -193,6 +226,10 @@ int fwd_padded(const void* q, const void* k, const void* v, void* o, float* lse,
       (st = rope_table(db, 0, Skv, D, rope_base, stream, &tab, "attn_fwd")) != ATTN_OK)
     return st;
   const int dt = dtype;  // kernel format codes: 0 fp32, 1 bf16, 2 fp16
+  xattn::KeySplit ks;
+  if (dtype != ATTN_F32 &&
+      (st = plan_splits_locked(db, B, Hq, Hkv, Sq, Skv, Dp, mask.p != nullptr, &ks)) != ATTN_OK)
+    return st;
   if ((e = xattn::launch_pack_heads(q, qp, B, Sq, Hq, D, Dp, tab, Skv - Sq, dt, stream)) !=
           hipSuccess ||
       (e = xattn::launch_pack_heads(k, kp, B, Skv, Hkv, D, Dp, tab, 0, dt, stream)) != hipSuccess ||
@@ -201,7 +238,7 @@ int fwd_padded(const void* q, const void* k, const void* v, void* o, float* lse,
     return hip_status(e, "attn_fwd: head-dim padding launch");
   if (dtype != ATTN_F32)
     e = xattn::launch_fwd16(qp, kp, vp, op, lse, B, Hq, Hkv, Sq, Skv, Dp, causal, scale, nullptr,
-                            dt, stream, nullptr, 0, mask);
+                            dt, stream, nullptr, 0, mask, ks);
   else
     e = xattn::launch_fwd_f32(qp, kp, vp, op, lse, B, Hq, Hkv, Sq, Skv, Dp, causal, scale,
                               nullptr, stream, mask);
@@ -266,12 +303,15 @@ int fwd(const char* fn, const void* q, const void* k, const void* v, void* o, fl
     }
   }
   hipError_t e;
-  if (dtype != ATTN_F32)
+  if (dtype != ATTN_F32) {
+    xattn::KeySplit ks;
+    if (int st = plan_splits(B, Hq, Hkv, Sq, Skv, D, mask.p != nullptr, &ks)) return st;
     e = xattn::launch_fwd16(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab, dtype,
-                            stream, nullptr, 0, mask);
-  else
+                            stream, nullptr, 0, mask, ks);
+  } else {
     e = xattn::launch_fwd_f32(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab,
                               stream, mask);
+  }
   return hip_status(e, "attn_fwd: kernel launch");
 }
 
@@ -458,8 +498,10 @@ int attn_prefill_kvcache(const void* q, const void* k_new, const void* v_new, vo
   hipError_t e = xattn::launch_cache_append(k_new, v_new, kcache, vcache, cache_lens, B, Sq, Hkv,
                                             D, max_seqlen, tab, stream);
   if (e != hipSuccess) return hip_status(e, "attn_prefill_kvcache: append launch");
+  xattn::KeySplit ks;
+  if (int st = plan_splits(B, Hq, Hkv, Sq, max_seqlen, D, false, &ks)) return st;
   e = xattn::launch_fwd16(q, kcache, vcache, o, lse, B, Hq, Hkv, Sq, max_seqlen, D, causal, scale,
-                          tab, ATTN_BF16, stream, cache_lens, max_seqlen);
+                          tab, ATTN_BF16, stream, cache_lens, max_seqlen, xattn::MaskView(), ks);
   return hip_status(e, "attn_prefill_kvcache: kernel launch");
 }
 

@@ -59,6 +59,9 @@
 #include "kernels.h"
 #include "lds.h"
 
+#include <algorithm>
+#include <cstdlib>
+
 namespace xattn {
 
 // Chunk swizzles (16-byte chunks, XORed with a function of the row).  LDS has
@@ -93,13 +96,14 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buf
 // The shared-mask variant with 4 or 8 heads per workgroup needs 40-48 KiB of
 // LDS, so three workgroups fit a CU if the registers allow three waves per
 // SIMD (<= 168 VGPRs, reached without spills; measured 6 % faster).
-template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB, int MASK>
+template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB, int MASK, bool SPLIT>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(MASK == 3 && HPW >= 4 ? 3 : 1))) void fwd16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Skv_all,
     const int* __restrict__ kv_lens, int kv_rows, float scale_log2,
-    const double2* __restrict__ tab, int n_qt, int n_bh, MaskView mask, float scale) {
+    const double2* __restrict__ tab, int n_qt, int n_bh, MaskView mask, float scale,
+    KeySplit ks_) {
   constexpr int BM = 128 * NQB, BN = 64, NP = BM / HPW;
   constexpr int KCH = D / 8;                 // 16-byte chunks per row
   constexpr int LD = BN * KCH / 256;         // 16-byte chunks per thread per tile (K and V each)
@@ -129,9 +133,15 @@ __attribute__((amdgpu_waves_per_eu(MASK == 3 && HPW >= 4 ? 3 : 1))) void fwd16_k
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
 
+  // block -> (query tile, key split, batch-head group); the group varies
+  // fastest (one XCD per group), query tiles heaviest first under causal
   const int bid = blockIdx.x;
-  const int qt = CAUSAL ? (n_qt - 1 - bid / n_bh) : (bid / n_bh);
   const int bh = bid % n_bh;
+  static_assert(!SPLIT || MASK == 0, "key splits are for unmasked launches");
+  const int nsplit = SPLIT ? ks_.n : 1;
+  const int split = (bid / n_bh) % nsplit;
+  const int qi = bid / n_bh / nsplit;
+  const int qt = CAUSAL ? (n_qt - 1 - qi) : qi;
   const int HG = Hq / HPW;
   const int b = bh / HG;
   const int h0 = (bh % HG) * HPW;
@@ -168,6 +178,14 @@ __attribute__((amdgpu_waves_per_eu(MASK == 3 && HPW >= 4 ? 3 : 1))) void fwd16_k
   if (CAUSAL) kv_end = min(Skv, min(p0 + NP, Sq) - 1 + off + 1);
   const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   const int first_q = p0 + off;  // smallest query position of the workgroup
+  // key tiles of this workgroup: all, or with nsplit > 1 the split-th of
+  // nsplit runs of ceil(ntiles / nsplit) tiles (possibly empty)
+  int t_lo = 0, t_hi = ntiles;
+  if constexpr (SPLIT) {
+    const int per = (ntiles + nsplit - 1) / nsplit;
+    t_lo = min(ntiles, split * per);
+    t_hi = min(ntiles, t_lo + per);
+  }
 
   // K and V of this (batch, kv head) through range-checked buffer resources:
   // rows at or past Skv read as zero, offsets are 32-bit.
@@ -317,8 +335,8 @@ __attribute__((amdgpu_waves_per_eu(MASK == 3 && HPW >= 4 ? 3 : 1))) void fwd16_k
           for (int e = 0; e < 4; ++e) cs[qb][ks][e] = tp[ks * 8 + e];
       }
     }
-    if (ntiles > 0) {
-      dma(0, Ks0, Vs0);
+    if (t_hi > t_lo) {
+      dma(t_lo * BN, Ks0, Vs0);
       if constexpr (MASK == 2) dma_rows<8>(rm, reinterpret_cast<u16*>(Mw), moff, 0u);
       if constexpr (MASK == 3)
         dma_rows<NI>(rm, reinterpret_cast<u16*>(Mx0 + w * NI * 256), moff, 0u);
@@ -389,7 +407,7 @@ __attribute__((amdgpu_waves_per_eu(MASK == 3 && HPW >= 4 ? 3 : 1))) void fwd16_k
           }
     };
     if constexpr (MASK == 1 && D == 64) load_mask();
-    if (t + 1 < ntiles) {
+    if (t + 1 < t_hi) {
       dma(k0 + BN, kn_, vn_);
       if constexpr (MASK == 3)
         dma_rows<NI>(rm, reinterpret_cast<u16*>(mn_ + w * NI * 256), moff, (uint32_t)(k0 + BN) * 4u);
@@ -434,7 +452,7 @@ __attribute__((amdgpu_waves_per_eu(MASK == 3 && HPW >= 4 ? 3 : 1))) void fwd16_k
       // the reads are done before the next tile's rows overwrite the area
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_sched_barrier(0);
-      if (t + 1 < ntiles)
+      if (t + 1 < t_hi)
         dma_rows<8>(rm, reinterpret_cast<u16*>(Mw), moff, (uint32_t)(k0 + BN) * 4u);
     }
     if constexpr (MASK != 0) {
@@ -525,9 +543,38 @@ __attribute__((amdgpu_waves_per_eu(MASK == 3 && HPW >= 4 ? 3 : 1))) void fwd16_k
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t_lo; t < t_hi; t += 2) {
     tile(t, Ks0, Vs0, Ks1, Vs1, Mx0, Mx1);
-    if (t + 1 < ntiles) tile(t + 1, Ks1, Vs1, Ks0, Vs0, Mx1, Mx0);
+    if (t + 1 < t_hi) tile(t + 1, Ks1, Vs1, Ks0, Vs0, Mx1, Mx0);
+  }
+
+  if constexpr (SPLIT) {
+    // partial result over this run of keys: O normalised by its own sum and
+    // its natural-log LSE (-inf when no key of the run is visible), at
+    // [row][split] with row = (b*Sq + pos)*Hq + h (O's row order), so one
+    // row's runs are contiguous for the combine kernel
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[qb]),
+                                                       __float_as_uint(l_run[qb]), false, false);
+      const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      if (qvalid[qb]) {
+        const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+        const long long slot = (((long long)b * Sq + pos[qb]) * Hq + hh[qb]) * nsplit + split;
+        float* op = ks_.o + slot * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const f32x4 x = {oacc[qb][db][4 * a] * inv, oacc[qb][db][4 * a + 1] * inv,
+                             oacc[qb][db][4 * a + 2] * inv, oacc[qb][db][4 * a + 3] * inv};
+            *reinterpret_cast<f32x4*>(op + db * 32 + 8 * a + 4 * g) = x;
+          }
+        if (g == 0)
+          ks_.l[slot] = (l_tot > 0.f) ? (m_run[qb] + __log2f(l_tot)) * kLn2 : -INFINITY;
+      }
+    }
+    return;
   }
 
 #pragma unroll
@@ -555,20 +602,71 @@ __attribute__((amdgpu_waves_per_eu(MASK == 3 && HPW >= 4 ? 3 : 1))) void fwd16_k
   }
 }
 
-template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB, int MASK>
+// Merge of the key splits: row r (O's row order) gets L = log sum_i exp(lse_i)
+// over its partial LSEs (empty runs carry -inf and weigh 0) and
+// O = sum_i exp(lse_i - L) O_i, stored in the input format; the LSE (nullable)
+// goes to [B, Hq, Sq].  A row with every run empty gets O = 0, LSE = -inf.
+// D / 4 threads per row, 16 bytes of each partial per thread.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fwd16_combine_kernel(const float* __restrict__ Op,
+                                                            const float* __restrict__ Lp,
+                                                            u16* __restrict__ O,
+                                                            float* __restrict__ LSE,
+                                                            long long rows, int Sq, int Hq,
+                                                            int ns) {
+  constexpr int TPR = D / 4;
+  const long long r = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int d = (threadIdx.x % TPR) * 4;
+  if (r >= rows) return;
+  const float* lp = Lp + r * ns;
+  float m2 = -INFINITY;  // in log2 units
+  for (int i = 0; i < ns; ++i) m2 = fmaxf(m2, lp[i] * kLog2e);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float L2 = -INFINITY;
+  if (m2 != -INFINITY) {
+    float sum = 0.f;
+    for (int i = 0; i < ns; ++i) sum += __builtin_amdgcn_exp2f(lp[i] * kLog2e - m2);
+    L2 = m2 + __log2f(sum);
+    for (int i = 0; i < ns; ++i) {
+      const float wgt = __builtin_amdgcn_exp2f(lp[i] * kLog2e - L2);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(Op + (r * ns + i) * D + d);
+      acc += wgt * x;
+    }
+  }
+  u32x2 pk;
+  pk[0] = Fmt16<T>::pack(acc[0], acc[1]);
+  pk[1] = Fmt16<T>::pack(acc[2], acc[3]);
+  *reinterpret_cast<u32x2*>(O + r * D + d) = pk;
+  if (LSE != nullptr && d == 0) {
+    const long long bs = r / Hq;  // b * Sq + pos
+    LSE[((bs / Sq) * Hq + r % Hq) * Sq + bs % Sq] = L2 * kLn2;
+  }
+}
+
+template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB, int MASK, bool SPLIT>
 static hipError_t go16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int Hq, int Hkv, int Sq, int Skv, const int* kv_lens, int kv_rows,
-                          float scale, const double2* tab, MaskView mask, hipStream_t stream) {
+                          float scale, const double2* tab, MaskView mask, KeySplit ks,
+                          hipStream_t stream) {
   constexpr int NP = 128 * NQB / HPW;
   const int n_qt = (Sq + NP - 1) / NP;
   const int n_bh = B * (Hq / HPW);
-  const long long nblocks = (long long)n_qt * n_bh;
+  const int nsplit = SPLIT ? ks.n : 1;
+  const long long nblocks = (long long)n_qt * n_bh * nsplit;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  fwd16_kernel<T, D, HPW, CAUSAL, ROPE, NQB, MASK>
+  fwd16_kernel<T, D, HPW, CAUSAL, ROPE, NQB, MASK, SPLIT>
       <<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
           static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v),
           static_cast<u16*>(o), lse, Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale * kLog2e, tab,
-          n_qt, n_bh, mask, scale);
+          n_qt, n_bh, mask, scale, ks);
+  if constexpr (SPLIT) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long rows = (long long)B * Sq * Hq;
+    constexpr int RPB = 256 / (D / 4);  // rows per block
+    fwd16_combine_kernel<T, D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream>>>(
+        ks.o, ks.l, static_cast<u16*>(o), lse, rows, Sq, Hq, nsplit);
+  }
   return hipGetLastError();
 }
 
@@ -579,7 +677,12 @@ static hipError_t go16(const void* q, const void* k, const void* v, void* o, flo
 template <typename T, int D, int HPW, bool CAUSAL, bool ROPE>
 static hipError_t go16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int Hq, int Hkv, int Sq, int Skv, const int* kv_lens, int kv_rows,
-                          float scale, const double2* tab, MaskView mask, hipStream_t stream) {
+                          float scale, const double2* tab, MaskView mask, KeySplit ks,
+                          hipStream_t stream) {
+  // an under-filled unmasked launch: one query block per wave, key splits
+  if (mask.p == nullptr && ks.n > 1)
+    return go16<T, D, HPW, CAUSAL, ROPE, 1, 0, true>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv,
+                                                     kv_lens, kv_rows, scale, tab, mask, ks, stream);
   if (mask.p != nullptr) {
     // staged mask rows for D = 64 when the loads can be 16-byte, the end of
     // the valid data (Skv keys into the last row) falls on a 16-byte boundary
@@ -592,54 +695,54 @@ static hipError_t go16(const void* q, const void* k, const void* v, void* o, flo
         // rows shared by the workgroup's heads when the mask is the same for all
         if constexpr (HPW >= 2)
           if (mask.hs == 0)
-            return go16<T, D, HPW, CAUSAL, ROPE, 1, 3>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv,
-                                                       kv_lens, kv_rows, scale, tab, mask, stream);
-        return go16<T, D, HPW, CAUSAL, ROPE, 1, 2>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
-                                                   kv_rows, scale, tab, mask, stream);
+            return go16<T, D, HPW, CAUSAL, ROPE, 1, 3, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv,
+                                                       kv_lens, kv_rows, scale, tab, mask, ks, stream);
+        return go16<T, D, HPW, CAUSAL, ROPE, 1, 2, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
+                                                   kv_rows, scale, tab, mask, ks, stream);
       }
     }
-    return go16<T, D, HPW, CAUSAL, ROPE, 1, 1>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
-                                               kv_rows, scale, tab, mask, stream);
+    return go16<T, D, HPW, CAUSAL, ROPE, 1, 1, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
+                                               kv_rows, scale, tab, mask, ks, stream);
   }
   if constexpr (D == 64) {
     const long long wg2 = (long long)((Sq + 256 / HPW - 1) / (256 / HPW)) * B * (Hq / HPW);
     if (wg2 >= 2 * 256)
-      return go16<T, D, HPW, CAUSAL, ROPE, 2, 0>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv,
-                                                     kv_lens, kv_rows, scale, tab, mask, stream);
+      return go16<T, D, HPW, CAUSAL, ROPE, 2, 0, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv,
+                                                     kv_lens, kv_rows, scale, tab, mask, ks, stream);
   }
-  return go16<T, D, HPW, CAUSAL, ROPE, 1, 0>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
-                                                 kv_rows, scale, tab, mask, stream);
+  return go16<T, D, HPW, CAUSAL, ROPE, 1, 0, false>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
+                                                 kv_rows, scale, tab, mask, ks, stream);
 }
 
 template <typename T, int D, bool CAUSAL, bool ROPE>
 static hipError_t pick_hpw(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Sq, int Skv, const int* kv_lens,
                            int kv_rows, float scale, const double2* tab, MaskView mask,
-                           hipStream_t stream) {
+                           KeySplit ks, hipStream_t stream) {
   const int G = Hq / Hkv;
   if (G % 8 == 0)
     return go16<T, D, 8, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
-                                       scale, tab, mask, stream);
+                                       scale, tab, mask, ks, stream);
   if (G % 4 == 0)
     return go16<T, D, 4, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
-                                       scale, tab, mask, stream);
+                                       scale, tab, mask, ks, stream);
   if (G % 2 == 0)
     return go16<T, D, 2, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
-                                       scale, tab, mask, stream);
+                                       scale, tab, mask, ks, stream);
   return go16<T, D, 1, CAUSAL, ROPE>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
-                                     scale, tab, mask, stream);
+                                     scale, tab, mask, ks, stream);
 }
 
 template <typename T>
 static hipError_t launch_fmt(const void* q, const void* k, const void* v, void* o, float* lse,
                              int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
                              float scale, const double2* rope_tab, hipStream_t stream,
-                             const int* kv_lens, int kv_rows, MaskView mask) {
+                             const int* kv_lens, int kv_rows, MaskView mask, KeySplit ks) {
   const bool rope = rope_tab != nullptr;
 #define XATTN_FWD16_CASE(DD, C, R)                                                         \
   if (D == DD && (causal != 0) == C && rope == R)                                          \
     return pick_hpw<T, DD, C, R>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale, \
-                                 rope_tab, mask, stream);
+                                 rope_tab, mask, ks, stream);
   XATTN_FWD16_CASE(64, false, false)
   XATTN_FWD16_CASE(64, true, false)
   XATTN_FWD16_CASE(64, false, true)
@@ -655,15 +758,45 @@ static hipError_t launch_fmt(const void* q, const void* k, const void* v, void* 
 hipError_t launch_fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                         int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
                         const double2* rope_tab, int dtype, hipStream_t stream,
-                        const int* kv_lens, int kv_rows, MaskView mask) {
+                        const int* kv_lens, int kv_rows, MaskView mask, KeySplit ks) {
   if (kv_lens == nullptr) kv_rows = Skv;
   if (dtype == 1)
     return launch_fmt<__bf16>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, rope_tab,
-                              stream, kv_lens, kv_rows, mask);
+                              stream, kv_lens, kv_rows, mask, ks);
   if (dtype == 2)
     return launch_fmt<_Float16>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, rope_tab,
-                                stream, kv_lens, kv_rows, mask);
+                                stream, kv_lens, kv_rows, mask, ks);
   return hipErrorInvalidValue;
+}
+
+int fwd16_key_splits(int B, int Hq, int Hkv, int Sq, int kv_rows, int D) {
+  const int G = Hq / Hkv;
+  const int HPW = G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+  const long long n_bh = (long long)B * (Hq / HPW);
+  const int tiles = (kv_rows + 63) / 64;
+  long long ns = 1;
+  const char* env = std::getenv("ATTN_FWD_SPLITS");
+  if (env != nullptr && *env != '\0') {
+    ns = std::atoll(env);
+  } else {
+    // the launch go16 makes without splits: two query blocks per wave
+    // (D = 64) when that still gives two workgroups per CU, else one.
+    // Measured (whole calls, 11 under-filled shapes from 16 to 256
+    // workgroups): a split costs a combine pass and the partials' traffic,
+    // which pays once a query tile has >= 32 key tiles and the launch has
+    // < 256 workgroups; then about 512 workgroups in total, >= 8 key tiles
+    // per split and <= 8 splits come within 4 % of the best count.
+    if (D == 64 && (long long)((Sq + 256 / HPW - 1) / (256 / HPW)) * n_bh >= 512) return 1;
+    const long long wg = (long long)((Sq + 128 / HPW - 1) / (128 / HPW)) * n_bh;
+    if (wg >= 256 || tiles < 32) return 1;
+    ns = std::min((512 + wg - 1) / wg, std::min((long long)(tiles / 8), 8LL));
+  }
+  return (int)std::max(1LL, std::min(ns, std::min(16LL, (long long)std::max(tiles, 1))));
+}
+
+size_t fwd16_split_ws_bytes(int B, int Hq, int Sq, int D, int ns) {
+  const size_t rows = (size_t)B * Sq * Hq;
+  return ((rows * ns * D * 4 + 255) & ~(size_t)255) + rows * ns * 4;
 }
 
 }  // namespace xattn

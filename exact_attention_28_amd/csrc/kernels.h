@@ -16,6 +16,25 @@ struct MaskView {
   bool vec = false;
 };
 
+// Key splits of an under-filled 16-bit forward launch (unmasked only): n runs
+// of key tiles per query tile, each writing its partial O (normalised by its
+// own sum) to o [rows][n][D] and its natural-log LSE to l [rows][n], fp32,
+// rows = B*Sq*Hq in O's row order; a combine pass merges them by log-sum-exp.
+// n = 1: no splits (o, l unused).
+struct KeySplit {
+  int n = 1;
+  float* o = nullptr;
+  float* l = nullptr;
+};
+
+// Split count for a forward launch of this shape (kv_rows: keys, or the cache
+// capacity): 1 when the unsplit launch has >= 256 workgroups or a query tile
+// has < 32 key tiles, else min(512 / workgroups, tiles / 8, 8).
+// ATTN_FWD_SPLITS in the environment overrides it (clamped to
+// [1, min(16, tiles)]).
+int fwd16_key_splits(int B, int Hq, int Hkv, int Sq, int kv_rows, int D);
+size_t fwd16_split_ws_bytes(int B, int Hq, int Sq, int D, int ns);
+
 // Prefill: q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D], o like q, lse [B,Hq,Sq] (nullable).
 // rope_tab: table rows for positions [0, Skv); query row i uses row Skv-Sq+i.
 // The 16-bit kernels (dtype 1 bf16, 2 fp16) rotate only the queries (keys
@@ -28,7 +47,7 @@ hipError_t launch_fwd16(const void* q, const void* k, const void* v, void* o, fl
                         int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
                         const double2* rope_tab, int dtype, hipStream_t stream,
                         const int* kv_lens = nullptr, int kv_rows = 0,
-                        MaskView mask = MaskView());
+                        MaskView mask = MaskView(), KeySplit ks = KeySplit());
 
 // Cache append: rows t < Sq of k_new/v_new [B,Sq,Hkv,D] (bf16) go to rows
 // L_b + t of kcache/vcache [B,rows,Hkv,D] with L_b = min(max(lens[b], 0),

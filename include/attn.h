@@ -23,7 +23,8 @@
  *  - Return value: ATTN_OK (0) or a negative attn_status_t; on error nothing is
  *    enqueued and attn_last_error() describes the problem.  Nothing throws
  *    across the ABI.
- *  - Library-owned device buffers (RoPE tables, rotated-K staging, the default
+ *  - Library-owned device buffers (RoPE tables, rotated-K staging, key-split
+ *    partials, the default
  *    decode and backward workspaces) are allocated on first need, grow only, and are kept per
  *    device until the process ends; calls that use them concurrently on
  *    different streams of one device must be ordered by the caller.
@@ -105,6 +106,14 @@ typedef enum {
  *   32-bit buffer offsets), ATTN_ERR_EMPTY_KV (Skv == 0),
  *   ATTN_ERR_HIP.  With rope_base > 0 and a 16-bit dtype, the call may allocate the
  *   library's rotated-K staging buffer (B*Skv*Hkv*D*2 bytes) and RoPE table.
+ * Key splits (16-bit, no mask): a launch with fewer than 256 workgroups whose
+ *   query tiles each have >= 32 key tiles of 64 splits each query tile's keys
+ *   into n <= 8 runs, one workgroup per run, and merges the runs' partial O
+ *   and LSE by log-sum-exp in a second kernel, as decode merges its splits
+ *   ([FD] fn combine_tile_outputs; the same result up to fp32 rounding
+ *   order); the partials live in a library-owned buffer of
+ *   B*Sq*Hq*n*(D+1)*4 bytes.  ATTN_FWD_SPLITS=n in the environment forces n
+ *   (1 disables splitting; clamped to 16 and to the key-tile count).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
              int Hkv, int Sq, int Skv, int D, int causal, float scale, float rope_base,
@@ -253,7 +262,8 @@ int attn_decode_splitkv(const void* q, const void* kcache, const void* vcache,
  *   causal 0 or 1; scale finite and > 0; rope_base > 0 enables RoPE (D even)
  * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP.  With RoPE the
  *   call uses the library's RoPE table for max_seqlen positions (built on the
- *   first such call on a stream and reused by the next ones).
+ *   first such call on a stream and reused by the next ones).  The attention
+ *   step splits keys as attn_fwd does, counting key tiles from max_seqlen.
  */
 int attn_prefill_kvcache(const void* q, const void* k_new, const void* v_new, void* kcache,
                          void* vcache, const int* cache_lens, void* o, float* lse, int B, int Hq,

@@ -1,8 +1,9 @@
 """Library calls captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
 
-A decode step (caller-owned workspace) and a forward with RoPE (after one
-eager call of the same shape, so that the library's table and key-staging
-buffers exist and nothing is allocated during capture) are captured once and
+A decode step (caller-owned workspace), a forward with RoPE and a forward
+whose keys are split over several workgroups (each after one eager call of
+the same shape, so that the library's table, key-staging and split buffers
+exist and nothing is allocated during capture) are captured once and
 replayed with new input contents, with eager work and synchronisation between
 the replays; every replay must give the eager call's bits.
 """
@@ -83,5 +84,31 @@ def test_rope_forward_in_a_graph():
         g.replay()
         torch.cuda.synchronize()
         o_ref, lse_ref = xa.attn_fwd(q, k, v, causal=True, rope_base=10000.0)
+        torch.cuda.synchronize()
+        assert _bits_equal(o, o_ref) and torch.equal(lse, lse_ref), rep
+
+
+def test_split_forward_in_a_graph():
+    """256 queries over 4096 keys on 8 heads: the forward splits the keys (8
+    runs) and merges them with a second kernel; both are captured."""
+    say("case graph split forward")
+    B, H, Sq, Skv, D = 1, 8, 256, 4096, 64
+    rng = np.random.default_rng(7)
+    q, k, v = (W.to_device(W.f32_to_bf16_bits(rng.standard_normal(s, dtype=np.float32)))
+               for s in ((B, Sq, H, D), (B, Skv, H, D), (B, Skv, H, D)))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
+    xa.attn_fwd(q, k, v, causal=True, o=o, lse=lse)  # buffers exist now
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        xa.attn_fwd(q, k, v, causal=True, o=o, lse=lse)
+    for rep in range(4):
+        q.copy_(W.to_device(W.f32_to_bf16_bits(rng.standard_normal((B, Sq, H, D),
+                                                                   dtype=np.float32))))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_ref, lse_ref = xa.attn_fwd(q, k, v, causal=True)
         torch.cuda.synchronize()
         assert _bits_equal(o, o_ref) and torch.equal(lse, lse_ref), rep

@@ -54,6 +54,12 @@
 //    (batch, head group) index is the fastest-varying part of the block index
 //    so that the workgroups of one head group land on one XCD (block i runs on
 //    XCD i mod 8) and share its L2.
+//  * Key splits (SPLIT instantiations, unmasked): when a launch would leave
+//    most CUs idle and each query tile has many key tiles, the keys of a query
+//    tile are split into runs handled by separate workgroups, each writing its
+//    partial O (normalised) and LSE; fwd16_combine_kernel merges them by
+//    log-sum-exp, as split-KV decoding merges its chunks (oxibonsai-model 0.1.4
+//    src/layers/flash_decode.rs, fn combine_tile_outputs).
 
 #include "common.h"
 #include "kernels.h"

@@ -45,10 +45,17 @@ def log(*a):
 
 
 def kernel_hash():
+    """Hash of the prefill kernel's sources with comments and whitespace
+    removed, so that a counter summary stays valid across comment edits and
+    goes stale when the code changes."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "exact_attention_28_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "exact_attention_28_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)  # block comments
+        src = re.sub(r"//[^\n]*", " ", src)                # line comments
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -5,28 +5,31 @@
 // block of 64 query rows, key/value blocks inside, a running row max m and row
 // sum l updated by fn online_softmax_update, the causal skip of key blocks that
 // lie wholly after the block's last query, and the final division by l.
-// Each query row is owned by a pair of lanes (each holds half of D), so the
-// row statistics stay in registers; K/V tiles are staged in LDS and read as
-// broadcasts.  fp32 has no dense MFMA advantage worth the fragment plumbing at
+// Each query row is owned by LPR lanes (each holds D / LPR of its columns;
+// the dot products are summed across them by DPP moves), so the row
+// statistics stay in registers; K/V tiles are staged in LDS and read as
+// broadcasts.  LPR = 2 (64 rows per workgroup) in general; LPR = 8 (16 rows)
+// or 16 (8 rows) when that grid would leave most CUs idle, which cuts each
+// lane's serial work per key several times for small problems.  fp32 has no dense MFMA advantage worth the fragment plumbing at
 // these sizes, so this path is plain VALU fp32.
 #include "common.h"
 #include "kernels.h"
 
 namespace xattn {
 
-template <int D, bool CAUSAL, bool ROPE>
+template <int D, bool CAUSAL, bool ROPE, int LPR>
 __global__ __launch_bounds__(128) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Skv,
     float scale_log2, const double2* __restrict__ tab, MaskView mask) {
-  constexpr int BQ = 64;
+  constexpr int BQ = 128 / LPR;
   constexpr int BK = (D == 64) ? 64 : 32;
-  constexpr int HD = D / 2;
+  constexpr int HD = D / LPR;  // columns per lane
   __shared__ float Ks[BK][D];
   __shared__ float Vs[BK][D];
 
   const int t = threadIdx.x;
-  const int r = t >> 1, half = t & 1;
+  const int r = t / LPR, half = t % LPR;  // row of the block, part of the row
   const int q0 = blockIdx.x * BQ;
   const int i = q0 + r;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -94,7 +97,9 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(
 #pragma unroll
       for (int d = 0; d < HD; ++d) part = fmaf(q[d], Ks[jj][half * HD + d], part);
       const int j = k0 + jj;
-      const float dot = part + __shfl_xor(part, 1);
+      // the row's lanes all get the same sum (DPP butterfly, same operand
+      // order on every lane), so their softmax statistics agree bit for bit
+      const float dot = group_sum<LPR>(part);
       float x = dot * scale_log2;
       if (mrow != nullptr && j < Skv) x = fmaf(dot, scale_log2, mrow[j] * kLog2e);
       if (j >= Skv || (CAUSAL && j > i + off)) x = -INFINITY;
@@ -127,15 +132,33 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(
   }
 }
 
+template <int D, bool CAUSAL, bool ROPE, int LPR>
+static hipError_t go_f32_lpr(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int Hq, int Hkv, int Sq, int Skv, float scale,
+                             const double2* tab, MaskView mask, hipStream_t stream) {
+  constexpr int BQ = 128 / LPR;
+  dim3 grid((Sq + BQ - 1) / BQ, Hq, B);
+  fwd_f32_kernel<D, CAUSAL, ROPE, LPR><<<grid, dim3(128), 0, stream>>>(
+      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+      static_cast<float*>(o), lse, Hq, Hkv, Sq, Skv, scale * kLog2e, tab, mask);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL, bool ROPE>
 static hipError_t go_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                          int Hq, int Hkv, int Sq, int Skv, float scale, const double2* tab,
                          MaskView mask, hipStream_t stream) {
-  dim3 grid((Sq + 63) / 64, Hq, B);
-  fwd_f32_kernel<D, CAUSAL, ROPE><<<grid, dim3(128), 0, stream>>>(
-      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-      static_cast<float*>(o), lse, Hq, Hkv, Sq, Skv, scale * kLog2e, tab, mask);
-  return hipGetLastError();
+  // fewer 64-row workgroups than CUs: 8 lanes per row (16 rows per
+  // workgroup), or 16 (8 rows) when there are fewer than a quarter as many
+  const long long wg = (long long)((Sq + 63) / 64) * Hq * B;
+  if (wg < 64)
+    return go_f32_lpr<D, CAUSAL, ROPE, 16>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab, mask,
+                                           stream);
+  if (wg < 256)
+    return go_f32_lpr<D, CAUSAL, ROPE, 8>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab, mask,
+                                          stream);
+  return go_f32_lpr<D, CAUSAL, ROPE, 2>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab, mask,
+                                        stream);
 }
 
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B,

@@ -103,6 +103,12 @@ F32_CASES = [  # B, Hq, Hkv, Sq, Skv, D, causal, rope
     (2, 2, 2, 65, 65, 128, False, 500.0),
     (1, 2, 1, 40, 20, 64, True, 0.0),  # rows with no visible key
     (1, 1, 1, 1, 1, 64, False, 0.0),
+    # the cases above have fewer than 64 workgroups of 64 rows (16 lanes per
+    # row); 64 to 255 run 8 lanes per row, >= 256 two
+    (1, 8, 8, 512, 256, 64, False, 0.0),
+    (1, 12, 4, 700, 900, 128, True, 500.0),
+    (2, 8, 2, 1024, 1024, 64, True, 10000.0),
+    (1, 16, 16, 1000, 512, 128, False, 0.0),
 ]
 
 

@@ -495,11 +495,13 @@ int attn_prefill_kvcache(const void* q, const void* k_new, const void* v_new, vo
         ATTN_OK)
       return st;
   }
+  // every buffer is in place before the first launch, so a failure leaves the
+  // caller's cache untouched
+  xattn::KeySplit ks;
+  if (int st = plan_splits(B, Hq, Hkv, Sq, max_seqlen, D, false, &ks)) return st;
   hipError_t e = xattn::launch_cache_append(k_new, v_new, kcache, vcache, cache_lens, B, Sq, Hkv,
                                             D, max_seqlen, tab, stream);
   if (e != hipSuccess) return hip_status(e, "attn_prefill_kvcache: append launch");
-  xattn::KeySplit ks;
-  if (int st = plan_splits(B, Hq, Hkv, Sq, max_seqlen, D, false, &ks)) return st;
   e = xattn::launch_fwd16(q, kcache, vcache, o, lse, B, Hq, Hkv, Sq, max_seqlen, D, causal, scale,
                           tab, ATTN_BF16, stream, cache_lens, max_seqlen, xattn::MaskView(), ks);
   return hip_status(e, "attn_prefill_kvcache: kernel launch");

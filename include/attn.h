@@ -24,10 +24,10 @@
  *    enqueued and attn_last_error() describes the problem.  Nothing throws
  *    across the ABI.
  *  - Library-owned device buffers (RoPE tables, rotated-K staging, key-split
- *    partials, the default
- *    decode and backward workspaces) are allocated on first need, grow only, and are kept per
- *    device until the process ends; calls that use them concurrently on
- *    different streams of one device must be ordered by the caller.
+ *    partials, the default decode and backward workspaces) are allocated on
+ *    first need, grow only, and are kept per device until the process ends;
+ *    calls that use them concurrently on different streams of one device
+ *    must be ordered by the caller.
  *  - The fp64 RoPE (cos, sin) table is built on the call's stream when a call
  *    needs positions, a head dim or a base that the table does not hold, or
  *    runs on another stream than the one that built it; otherwise it is

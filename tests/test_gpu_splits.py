@@ -44,6 +44,8 @@ CASES = [  # B, Hq, Hkv, Sq, Skv, D, causal, rope, dtype
     (1, 2, 1, 70, 20, 64, True, 0.0, "bf16"),          # rows with no visible key
     (1, 4, 4, 64, 1000, 128, False, 0.0, "bf16"),      # D = 128, long keys
     (2, 6, 3, 33, 500, 64, True, 0.0, "f16"),          # fp16, 2 heads per kv head
+    (1, 1, 1, 1, 8192, 64, False, 0.0, "bf16"),        # one query row, long keys
+    (1, 32, 2, 64, 3000, 64, True, 10000.0, "bf16"),   # 16 query heads per kv head
 ]
 
 

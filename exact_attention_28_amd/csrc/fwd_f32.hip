@@ -8,25 +8,46 @@
 // Each query row is owned by LPR lanes (each holds D / LPR of its columns;
 // the dot products are summed across them by DPP moves), so the row
 // statistics stay in registers; K/V tiles are staged in LDS and read as
-// broadcasts.  LPR = 2 (64 rows per workgroup) in general; LPR = 8 (16 rows)
-// or 16 (8 rows) when that grid would leave most CUs idle, which cuts each
-// lane's serial work per key several times for small problems.  fp32 has no dense MFMA advantage worth the fragment plumbing at
-// these sizes, so this path is plain VALU fp32.
+// broadcasts.  LPR = 4 (32 rows per workgroup) in general; LPR = 8 (16 rows)
+// or 16 (8 rows) when a grid of 64-row blocks would leave most CUs idle, which
+// cuts each lane's serial work per key several times for small problems.  fp32 has no
+// dense MFMA advantage worth the fragment plumbing at these sizes, so this
+// path is plain VALU fp32.
 #include "common.h"
 #include "kernels.h"
 
 namespace xattn {
 
-template <int D, bool CAUSAL, bool ROPE, int LPR>
+// LDS of one workgroup: a key and a value block, and with a mask its tile
+// (rows padded by one entry so that the rows one wave reads sit in different
+// banks).  The unmasked kernels carry no mask tile (32 KiB of LDS).
+template <int BQ, int BK, int D, bool MASK>
+struct alignas(16) F32Tiles {
+  float k[BK][D];
+  float v[BK][D];
+  float m[BQ][BK + 1];
+};
+template <int BQ, int BK, int D>
+struct alignas(16) F32Tiles<BQ, BK, D, false> {
+  float k[BK][D];
+  float v[BK][D];
+};
+
+template <int D, bool CAUSAL, bool ROPE, int LPR, bool MASK>
 __global__ __launch_bounds__(128) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Skv,
     float scale_log2, const double2* __restrict__ tab, MaskView mask) {
   constexpr int BQ = 128 / LPR;
   constexpr int BK = (D == 64) ? 64 : 32;
-  constexpr int HD = D / LPR;  // columns per lane
-  __shared__ float Ks[BK][D];
-  __shared__ float Vs[BK][D];
+  constexpr int HD = D / LPR;        // columns per lane
+  constexpr int CPR = D / 4;         // 16-byte chunks per key row
+  constexpr int NCH = BK * CPR / 128;  // chunks of K (and of V) per thread and block
+  constexpr int MPT = BQ * BK / 128;   // mask entries per thread and block
+  static_assert(NCH * 128 == BK * CPR && MPT * 128 == BQ * BK, "block shape");
+  __shared__ F32Tiles<BQ, BK, D, MASK> sm;
+  auto& Ks = sm.k;
+  auto& Vs = sm.v;
 
   const int t = threadIdx.x;
   const int r = t / LPR, half = t % LPR;  // row of the block, part of the row
@@ -36,18 +57,82 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(
   const int g = h / (Hq / Hkv);
   const int off = Skv - Sq;  // bottom-right causal alignment
 
+  // Key/value blocks (and mask tiles) pass through registers into LDS, every
+  // load of a block issued before the first wait.  With 8 or 16 lanes per row
+  // (grids too small to hide latency by occupancy) the next block is fetched
+  // while the current one is used; with 4 the loads of a block are issued
+  // before the barrier that precedes its staging, so that the registers are
+  // free during the arithmetic.  Rows past Skv are zero (mask entries 0).
+  constexpr bool kAhead = LPR >= 8;
+  float4 kr[NCH], vr[NCH];
+  float mr[MASK ? MPT : 1];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int e = t + 128 * c;
+      const int j = k0 + e / CPR;
+      const long long src = (((long long)b * Skv + min(j, Skv - 1)) * Hkv + g) * D + 4 * (e % CPR);
+      kr[c] = *reinterpret_cast<const float4*>(K + src);
+      vr[c] = *reinterpret_cast<const float4*>(V + src);
+    }
+    if constexpr (MASK) {
+#pragma unroll
+      for (int c = 0; c < MPT; ++c) {
+        const int e = t + 128 * c;
+        const int mi = min(q0 + e / BK, Sq - 1), j = k0 + e % BK;
+        mr[c] = (j < Skv) ? mask.p[b * mask.bs + h * mask.hs + (long long)mi * mask.rs + j] : 0.f;
+      }
+    }
+  };
+  auto stage = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int e = t + 128 * c;
+      const int jj = e / CPR, cc = e % CPR;
+      const int j = k0 + jj;
+      float4 kv = kr[c], vv = vr[c];
+      if (j >= Skv) {
+        kv = make_float4(0.f, 0.f, 0.f, 0.f);
+        vv = kv;
+      } else if (ROPE) {
+        const double2* trow = tab + (long long)j * (D / 2) + 2 * cc;
+        double r0, r1;
+        rotate_pair((double)kv.x, (double)kv.y, trow[0], r0, r1);
+        kv.x = (float)r0;
+        kv.y = (float)r1;
+        rotate_pair((double)kv.z, (double)kv.w, trow[1], r0, r1);
+        kv.z = (float)r0;
+        kv.w = (float)r1;
+      }
+      *reinterpret_cast<float4*>(&Ks[jj][4 * cc]) = kv;
+      *reinterpret_cast<float4*>(&Vs[jj][4 * cc]) = vv;
+    }
+    if constexpr (MASK) {
+#pragma unroll
+      for (int c = 0; c < MPT; ++c) {
+        const int e = t + 128 * c;
+        sm.m[e / BK][e % BK] = mr[c];
+      }
+    }
+  };
+
   float q[HD], o[HD];
   {
-    const long long base = (((long long)b * Sq + (i < Sq ? i : 0)) * Hq + h) * D + half * HD;
+    const long long base = (((long long)b * Sq + min(i, Sq - 1)) * Hq + h) * D + half * HD;
 #pragma unroll
-    for (int d = 0; d < HD; ++d) q[d] = (i < Sq) ? Q[base + d] : 0.f;
-    if (ROPE && i < Sq) {
-      const int pos = off + i;
+    for (int d = 0; d < HD; d += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(Q + base + d);
+      q[d] = x.x;
+      q[d + 1] = x.y;
+      q[d + 2] = x.z;
+      q[d + 3] = x.w;
+    }
+    if (ROPE) {
+      const double2* trow = tab + (long long)(off + min(i, Sq - 1)) * (D / 2) + half * HD / 2;
 #pragma unroll
       for (int d = 0; d < HD; d += 2) {
         double r0, r1;
-        rotate_pair((double)q[d], (double)q[d + 1], tab[(long long)pos * (D / 2) + (half * HD + d) / 2],
-                    r0, r1);
+        rotate_pair((double)q[d], (double)q[d + 1], trow[d / 2], r0, r1);
         q[d] = (float)r0;
         q[d + 1] = (float)r1;
       }
@@ -56,38 +141,19 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(
     for (int d = 0; d < HD; ++d) o[d] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  // this row's additive mask (the [WH] compute_block_scores mask term), or null
-  const float* mrow =
-      mask.p ? mask.p + b * mask.bs + h * mask.hs + (long long)(i < Sq ? i : 0) * mask.rs : nullptr;
 
   int kv_end = Skv;
   if (CAUSAL) {
     const int last_q = min(q0 + BQ, Sq) - 1;
     kv_end = min(Skv, last_q + off + 1);
   }
+  if (kAhead && kv_end > 0) fetch(0);
   for (int k0 = 0; k0 < kv_end; k0 += BK) {
+    if (!kAhead) fetch(k0);
+    __syncthreads();  // every wave is done with the previous block
+    stage(k0);
     __syncthreads();
-    // stage the key/value block (rows past Skv are zero)
-    for (int e = t; e < BK * D / 2; e += 128) {
-      const int jj = e / (D / 2), pr = e % (D / 2);
-      const int j = k0 + jj;
-      float2 kv = make_float2(0.f, 0.f), vv = make_float2(0.f, 0.f);
-      if (j < Skv) {
-        const long long src = (((long long)b * Skv + j) * Hkv + g) * D + 2 * pr;
-        kv = *reinterpret_cast<const float2*>(K + src);
-        vv = *reinterpret_cast<const float2*>(V + src);
-        if (ROPE) {
-          double r0, r1;
-          rotate_pair((double)kv.x, (double)kv.y, tab[(long long)j * (D / 2) + pr], r0, r1);
-          kv = make_float2((float)r0, (float)r1);
-        }
-      }
-      Ks[jj][2 * pr] = kv.x;
-      Ks[jj][2 * pr + 1] = kv.y;
-      Vs[jj][2 * pr] = vv.x;
-      Vs[jj][2 * pr + 1] = vv.y;
-    }
-    __syncthreads();
+    if (kAhead && k0 + BK < kv_end) fetch(k0 + BK);
 
     float s[BK];
     float bmax = -INFINITY;
@@ -101,10 +167,17 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(
       // order on every lane), so their softmax statistics agree bit for bit
       const float dot = group_sum<LPR>(part);
       float x = dot * scale_log2;
-      if (mrow != nullptr && j < Skv) x = fmaf(dot, scale_log2, mrow[j] * kLog2e);
+      // the row's additive mask (the [WH] compute_block_scores mask term)
+      if constexpr (MASK) {
+        if (j < Skv) x = fmaf(dot, scale_log2, sm.m[r][jj] * kLog2e);
+      }
       if (j >= Skv || (CAUSAL && j > i + off)) x = -INFINITY;
       s[jj] = x;
       bmax = fmaxf(bmax, x);
+      // key-major order: with 32 or more columns per lane the compiler may
+      // otherwise turn the loop inside out (four columns of every key at a
+      // time) and then wait for each LDS read before the next
+      if constexpr (HD >= 32) asm volatile("" ::: "memory");
     }
     const float m_new = fmaxf(m, bmax);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -118,6 +191,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(
       l += p;
 #pragma unroll
       for (int d = 0; d < HD; ++d) o[d] = fmaf(p, Vs[jj][half * HD + d], o[d]);
+      if constexpr (HD >= 32) asm volatile("" ::: "memory");  // key-major, as above
     }
     m = m_new;
   }
@@ -138,9 +212,15 @@ static hipError_t go_f32_lpr(const void* q, const void* k, const void* v, void* 
                              const double2* tab, MaskView mask, hipStream_t stream) {
   constexpr int BQ = 128 / LPR;
   dim3 grid((Sq + BQ - 1) / BQ, Hq, B);
-  fwd_f32_kernel<D, CAUSAL, ROPE, LPR><<<grid, dim3(128), 0, stream>>>(
-      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-      static_cast<float*>(o), lse, Hq, Hkv, Sq, Skv, scale * kLog2e, tab, mask);
+  const float* qf = static_cast<const float*>(q);
+  const float* kf = static_cast<const float*>(k);
+  const float* vf = static_cast<const float*>(v);
+  if (mask.p != nullptr)
+    fwd_f32_kernel<D, CAUSAL, ROPE, LPR, true><<<grid, dim3(128), 0, stream>>>(
+        qf, kf, vf, static_cast<float*>(o), lse, Hq, Hkv, Sq, Skv, scale * kLog2e, tab, mask);
+  else
+    fwd_f32_kernel<D, CAUSAL, ROPE, LPR, false><<<grid, dim3(128), 0, stream>>>(
+        qf, kf, vf, static_cast<float*>(o), lse, Hq, Hkv, Sq, Skv, scale * kLog2e, tab, mask);
   return hipGetLastError();
 }
 
@@ -148,8 +228,8 @@ template <int D, bool CAUSAL, bool ROPE>
 static hipError_t go_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                          int Hq, int Hkv, int Sq, int Skv, float scale, const double2* tab,
                          MaskView mask, hipStream_t stream) {
-  // fewer 64-row workgroups than CUs: 8 lanes per row (16 rows per
-  // workgroup), or 16 (8 rows) when there are fewer than a quarter as many
+  // counted in 64-row blocks: fewer than there are CUs, 8 lanes per row (16
+  // rows per workgroup), or 16 (8 rows) below a quarter of that; else 4 (32)
   const long long wg = (long long)((Sq + 63) / 64) * Hq * B;
   if (wg < 64)
     return go_f32_lpr<D, CAUSAL, ROPE, 16>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab, mask,
@@ -157,7 +237,7 @@ static hipError_t go_f32(const void* q, const void* k, const void* v, void* o, f
   if (wg < 256)
     return go_f32_lpr<D, CAUSAL, ROPE, 8>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab, mask,
                                           stream);
-  return go_f32_lpr<D, CAUSAL, ROPE, 2>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab, mask,
+  return go_f32_lpr<D, CAUSAL, ROPE, 4>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, scale, tab, mask,
                                         stream);
 }
 

@@ -104,7 +104,7 @@ def _mask_shape(kind, B, Hq, Sq, Skv):
 def test_masked_bf16(case):
     B, Hq, Hkv, Sq, Skv, D, causal, rope, kind = case
     say("case mask bf16", case)
-    rng = np.random.default_rng(abs(hash(case)) % 2 ** 32)
+    rng = np.random.default_rng(W.case_seed(case))
     q = W.f32_to_bf16_bits(rng.standard_normal((B, Sq, Hq, D), dtype=np.float32))
     k = W.f32_to_bf16_bits(rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32))
     v = W.f32_to_bf16_bits(rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32))
@@ -117,12 +117,18 @@ def test_masked_bf16(case):
 
 @pytest.mark.parametrize("case", [(2, 4, 2, 100, 150, 64, True, 0.0, "bh"),
                                   (1, 2, 1, 33, 70, 128, False, 10000.0, "s"),
-                                  (2, 2, 2, 45, 80, 24, False, 0.0, "kp")],
+                                  (2, 2, 2, 45, 80, 24, False, 0.0, "kp"),
+                                  # 16 lanes per row over five key blocks; 8 lanes;
+                                  # 4 lanes, ragged rows and keys, at D 64 and 128
+                                  (1, 1, 1, 100, 300, 64, False, 0.0, "s"),
+                                  (1, 16, 16, 200, 300, 128, True, 10000.0, "h"),
+                                  (2, 8, 2, 1000, 1111, 64, True, 10000.0, "bh"),
+                                  (1, 16, 4, 1000, 300, 128, False, 0.0, "kp")],
                          ids=str)
 def test_masked_f32(case):
     B, Hq, Hkv, Sq, Skv, D, causal, rope, kind = case
     say("case mask f32", case)
-    rng = np.random.default_rng(abs(hash(case)) % 2 ** 32)
+    rng = np.random.default_rng(W.case_seed(case))
     q = rng.standard_normal((B, Sq, Hq, D), dtype=np.float32)
     k = rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32)
     v = rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32)

@@ -13,6 +13,7 @@ for each sequence b its K rows [0, L_b) followed by its V rows [0, L_b); cache
 rows at and beyond L_b hold a quiet-NaN canary so that any read past the length
 shows up in the output.
 """
+import zlib
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -84,6 +85,12 @@ C3 = Prefill("whisper_encoder_s1500", 8, 20, 20, 1500, 1500, 64, False, 0.0, "bf
 C4 = Prefill("lfm2_gqa_prefill_s4096", 4, 32, 8, 4096, 4096, 64, True, 10000.0, "bf16", 1004)
 C5 = Decode("splitkv_decode_s32768", 16, 32, 8, 128, 32768, 1024, 32768, 1005)
 PREFILL = (C1, C2N, C2C, C3, C4)
+
+
+def case_seed(case):
+    """A seed for a test case's inputs that is the same in every process
+    (Python's hash() of a string changes from one interpreter to the next)."""
+    return zlib.crc32(repr(case).encode())
 
 
 def f32_to_bf16_bits(x):

@@ -16,7 +16,10 @@
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    never frees caller memory.  Tensors are dense and contiguous.
+ *    never frees caller memory.  Tensors are dense and contiguous, and start
+ *    16-byte aligned (as hipMalloc and torch allocations, and row views of
+ *    them at D = 64 or 128, do): the kernels move rows in 16-byte loads and
+ *    stores.  This is a precondition, not checked.
  *  - Calls are asynchronous on `stream` (0 = the null stream): arguments are
  *    validated synchronously on the host before anything is enqueued, then
  *    the kernels are launched and the call returns without synchronising.

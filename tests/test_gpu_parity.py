@@ -112,6 +112,8 @@ F32_CASES = [  # B, Hq, Hkv, Sq, Skv, D, causal, rope
     (1, 1, 1, 100, 333, 64, False, 0.0),  # 16 lanes, 6 key blocks, ragged tail
     (4, 8, 8, 1000, 777, 64, False, 0.0),  # four lanes, ragged rows and keys
     (2, 8, 4, 1024, 1100, 128, True, 10000.0),
+    (1, 16, 2, 1100, 1, 64, False, 0.0),  # four lanes, one key
+    (1, 16, 16, 1030, 1000, 128, True, 0.0),  # four lanes, first 30 rows see no key
 ]
 
 

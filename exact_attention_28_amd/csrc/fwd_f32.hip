@@ -91,18 +91,22 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(
       const int jj = e / CPR, cc = e % CPR;
       const int j = k0 + jj;
       float4 kv = kr[c], vv = vr[c];
+      if (ROPE) {
+        // table rows read unconditionally (clamped), so that every load of
+        // the block is issued before the first rotation waits
+        const double2* trow = tab + (long long)min(j, Skv - 1) * (D / 2) + 2 * cc;
+        const double2 cs0 = trow[0], cs1 = trow[1];
+        double r0, r1;
+        rotate_pair((double)kv.x, (double)kv.y, cs0, r0, r1);
+        kv.x = (float)r0;
+        kv.y = (float)r1;
+        rotate_pair((double)kv.z, (double)kv.w, cs1, r0, r1);
+        kv.z = (float)r0;
+        kv.w = (float)r1;
+      }
       if (j >= Skv) {
         kv = make_float4(0.f, 0.f, 0.f, 0.f);
         vv = kv;
-      } else if (ROPE) {
-        const double2* trow = tab + (long long)j * (D / 2) + 2 * cc;
-        double r0, r1;
-        rotate_pair((double)kv.x, (double)kv.y, trow[0], r0, r1);
-        kv.x = (float)r0;
-        kv.y = (float)r1;
-        rotate_pair((double)kv.z, (double)kv.w, trow[1], r0, r1);
-        kv.z = (float)r0;
-        kv.w = (float)r1;
       }
       *reinterpret_cast<float4*>(&Ks[jj][4 * cc]) = kv;
       *reinterpret_cast<float4*>(&Vs[jj][4 * cc]) = vv;

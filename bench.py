@@ -10,10 +10,18 @@ One step is one pass of the whole path on resident synthetic inputs:
     4, 8, 16, 32, 64 before the timed region.
 
 Printed: one JSON line.  `value` is the prefill throughput in TFLOP/s
-(algorithmic flops 4*B*Hq*S*S*D/2 over the event-timed attn_fwd call); the
-decode KV-read bandwidth and both fractions of peak sit beside it.  The
-`roofline` object is for the dominant kernel (the fused prefill kernel),
-timed alone with HIP events on its stream.
+(algorithmic flops 4*B*Hq*S*S*D/2 over the median event-timed attn_fwd call
+of the timed steps); the decode KV-read bandwidth (median of 50 calls, each
+after a 512 MiB flush write) and both fractions of peak sit beside it.  The
+`roofline` object is for the dominant kernel, the fused RoPE attention
+kernel of the headline call, timed by HIP events that the library records
+on the call's stream around that kernel's launch (attn_profile_begin/_end).
+
+Modes for rocprofv3 runs (each launches one thing only): --profile-kernel
+REPS [--profile-workload NAME] (production attn_fwd calls on a prefill
+workload, then a calibration copy), --profile-decode REPS [--profile-splits
+N], --profile-backward REPS; and the summary writers --traffic-summary and
+--counters-summary.
 """
 import argparse
 import hashlib
@@ -37,6 +45,11 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 METRIC = "attention fwd TFLOP/s + decode KV GB/s, as % of MI355X MFMA/HBM peak"
 KERNEL_SOURCES = ("fwd16.hip", "common.h", "lds.h")
+# the attention kernel of the headline LFM2 prefill call (template arguments:
+# element type, head dim, query heads per workgroup, causal, fused query RoPE,
+# query blocks per wave, mask kind, key split)
+KERNEL_LABEL = "fwd16_kernel<__bf16, D=64, HPW=4, CAUSAL=1, ROPE=1, NQB=2, MASK=0, SPLIT=0>"
+KERNEL_LABEL_NOROPE = "fwd16_kernel<__bf16, D=64, HPW=4, CAUSAL=1, ROPE=0, NQB=2, MASK=0, SPLIT=0>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd16_lfm2_gqa_prefill_s4096_traffic.txt")
 
 
@@ -77,31 +90,33 @@ def read_traffic(launch_flops_bytes):
         return None
 
 
-def timed(fn, reps, stream):
-    """Mean duration (ms) of fn() over reps, bracketed by HIP events on stream."""
+def timed(fn, reps, stream, between=None):
+    """Median duration (ms) of fn() over reps, each bracketed by HIP events on
+    stream; `between` (e.g. a cache flush) runs before each repetition,
+    outside the events."""
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     for i in range(reps):
+        if between is not None:
+            between()
         starts[i].record(stream)
         fn()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    return float(np.median([s.elapsed_time(e) for s, e in zip(starts, ends)]))
 
 
-def timed_queued(fn, reps, stream):
-    """Mean GPU time (ms) per call of fn over reps back-to-back calls.  A spin
-    kernel (about 1.5 ms) runs first, so the host has enqueued the calls
-    before the first one starts: for calls shorter than their host-side
-    launch cost, the events then bracket GPU time, not launch overhead."""
-    torch.cuda._sleep(3_000_000)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+def kernel_times(fn, reps):
+    """Per-launch GPU times (ms) of the attention kernel of `reps` forward
+    calls fn(), from the library's event pairs around that launch (the
+    attn_profile session of the C ABI): the RoPE table build and key rotation
+    of a call are outside them."""
+    xa.attn_profile_begin()
     for _ in range(reps):
         fn()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    t = xa.attn_profile_end(cap=reps)
+    assert len(t) == reps, (len(t), reps)
+    return t
 
 
 def settle(fn, seconds):
@@ -139,7 +154,10 @@ def cpu_baseline(prefill, dec_inputs, budget_s):
     the budget are spent (or the workload is done), then whole passes of the
     decode workload for the last third (at least one pass)."""
     import oracle
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    # the GPU host gives one GPU's job a share of 16 cores, whatever the
+    # affinity mask shows; both numbers are reported
+    avail = len(os.sched_getaffinity(0))
+    threads = max(1, min(16, avail))
     cfg = W.C4
     q, k, v = prefill
     n_units = cfg.B * cfg.Hq
@@ -153,7 +171,8 @@ def cpu_baseline(prefill, dec_inputs, budget_s):
         done += len(units)
     t_pre = time.perf_counter() - t0
     flops = cfg.flops / n_units * done
-    out = {"value": flops / t_pre / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    out = {"value": flops / t_pre / 1e12, "unit": "TFLOP/s", "cores": threads,
+           "cores_in_affinity_mask": avail, "kind": "oracle",
            "sample": f"LFM2 GQA prefill, {done} of {n_units} (batch, head) units "
                      f"(all 4096 query rows each), {t_pre:.1f} s",
            "host": host_cpu()}
@@ -175,26 +194,27 @@ def cpu_baseline(prefill, dec_inputs, budget_s):
 
 
 COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
+FLUSH_BYTES = 512 << 20  # written between decode repetitions (twice the 256 MiB MALL)
 
 
 def profile_kernel(reps, workload):
-    """For counter runs: `reps` launches of the prefill kernel alone (Q and K
-    rotated beforehand when the workload has RoPE) on the named prefill
-    workload (default the LFM2 prefill), then `reps` launches of a plain
-    elementwise copy of COPY_BYTES (dst = src + 0) for calibration."""
+    """For trace and counter runs: `reps` production attn_fwd calls on the
+    named prefill workload (default the LFM2 prefill: RoPE table once, then
+    per call the key rotation and the fused attention kernel), after one
+    untimed call, then `reps` launches of a plain elementwise copy of
+    COPY_BYTES (dst = src + 0) for calibration."""
     pc = {c.name: c for c in W.PREFILL}[workload]
     q_np, k_np, v_np = W.prefill_inputs(pc)
     q, k, v = W.to_device(q_np), W.to_device(k_np), W.to_device(v_np)
-    if pc.rope_base > 0:
-        xa.rope_apply(q, 0, pc.rope_base)
-        xa.rope_apply(k, 0, pc.rope_base)
     o = torch.empty_like(q)
     lse = torch.empty((pc.B, pc.Hq, pc.Sq), dtype=torch.float32, device="cuda")
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    xa.attn_fwd(q, k, v, causal=pc.causal, scale=pc.scale, rope_base=pc.rope_base, o=o, lse=lse)
     torch.cuda.synchronize()
     for _ in range(reps):
-        xa.attn_fwd(q, k, v, causal=pc.causal, scale=pc.scale, o=o, lse=lse)
+        xa.attn_fwd(q, k, v, causal=pc.causal, scale=pc.scale, rope_base=pc.rope_base, o=o,
+                    lse=lse)
     torch.cuda.synchronize()
     for _ in range(reps):
         torch.add(src, 0.0, out=dst)
@@ -202,22 +222,22 @@ def profile_kernel(reps, workload):
     log("profile-kernel done")
 
 
-def profile_decode(reps):
-    """For counter runs: `reps` split-KV decode calls (split + merge, 16
-    splits) on the decode workload, then `reps` launches of the calibration
-    copy."""
+def profile_decode(reps, ns=16):
+    """For trace and counter runs: `reps` split-KV decode calls (split +
+    merge, `ns` splits) on the decode workload, then `reps` launches of the
+    calibration copy."""
     dc = W.C5
     dq_np, kc_np, vc_np, sl_np = W.decode_inputs(dc)
     dq, kc, vc = W.to_device(dq_np), W.to_device(kc_np), W.to_device(vc_np)
     sl = torch.from_numpy(sl_np).cuda()
     do = torch.empty_like(dq)
-    ws = torch.empty(xa.attn_decode_workspace_bytes(dc.B, dc.Hq, dc.D, 16), dtype=torch.uint8,
+    ws = torch.empty(xa.attn_decode_workspace_bytes(dc.B, dc.Hq, dc.D, ns), dtype=torch.uint8,
                      device="cuda")
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(reps):
-        xa.attn_decode_splitkv(dq, kc, vc, sl, 16, scale=dc.scale, o=do, workspace=ws)
+        xa.attn_decode_splitkv(dq, kc, vc, sl, ns, scale=dc.scale, o=do, workspace=ws)
     torch.cuda.synchronize()
     for _ in range(reps):
         torch.add(src, 0.0, out=dst)
@@ -302,8 +322,8 @@ def traffic_summary(fetch_csv, write_csv, out_path, cmds):
     fetch_b, write_b = fe["attn"] * f_fac * 1024, wr["attn"] * w_fac * 1024
     pc = W.C4
     lines = [
-        "# HBM traffic of the prefill kernel fwd16_kernel<bf16,D=64,HPW=4,causal> on the LFM2",
-        "# prefill workload (B4 Hq32 Hkv8 S4096 D64 bf16, Q/K pre-rotated), per launch.",
+        f"# HBM traffic of the prefill kernel {KERNEL_LABEL} on the LFM2",
+        "# prefill workload (B4 Hq32 Hkv8 S4096 D64 bf16, causal, RoPE; production calls), per launch.",
         "# Counters are KiB per dispatch; each is scaled by expected/measured for a plain",
         f"# elementwise copy of {COPY_BYTES} bytes (read {COPY_BYTES}, write {COPY_BYTES}).",
         "# Commands (from the repository root, TMPDIR=/tmp):",
@@ -345,6 +365,8 @@ def main():
                     help="command line recorded in the traffic summary (repeatable)")
     ap.add_argument("--profile-decode", type=int, default=0, metavar="REPS",
                     help="only run the split-KV decode REPS times, then a calibration copy")
+    ap.add_argument("--profile-splits", type=int, default=16,
+                    help="split count of --profile-decode")
     ap.add_argument("--profile-backward", type=int, default=0, metavar="REPS",
                     help="only run the LFM2 prefill backward REPS times")
     ap.add_argument("--counters-summary", nargs=4, metavar=("CSV", "MATCH", "OUT", "TITLE"),
@@ -366,7 +388,7 @@ def main():
         profile_kernel(args.profile_kernel, args.profile_workload)
         return
     if args.profile_decode:
-        profile_decode(args.profile_decode)
+        profile_decode(args.profile_decode, args.profile_splits)
         return
     if args.profile_backward:
         profile_backward(args.profile_backward)
@@ -401,14 +423,21 @@ def main():
     log("settle")
     n_settle = settle(lambda: (prefill(), decode(dc.splits[0])), args.settle)
 
-    # ---- warmup, and the split count for the decode half (outside the timed region)
+    # ---- warmup, and the split count for the decode half (outside the timed
+    # region): each count timed as the decode record below is, median of
+    # calls with a 512 MiB flush write before each
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    def flush_caches():
+        flush.fill_(1.0)
+
     log("warmup")
     for _ in range(max(args.warmup, 1)):
         prefill()
         for ns in dc.splits:
             decode(ns)
     torch.cuda.synchronize()
-    split_ms = {ns: timed(lambda: decode(ns), 20, stream) for ns in dc.splits}
+    split_ms = {ns: timed(lambda: decode(ns), 15, stream, flush_caches) for ns in dc.splits}
     best_ns = min(split_ms, key=split_ms.get)
     log("decode ms per split count:", {k_: round(v_, 4) for k_, v_ in split_ms.items()})
 
@@ -424,23 +453,36 @@ def main():
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    pre_all = [e[0].elapsed_time(e[1]) for e in ev]
+    pre_ms = float(np.median(pre_all))
+    step_dec_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
     ms_per_step = wall * 1e3 / args.steps
     pre_tflops = pc.flops / (pre_ms * 1e-3) / 1e12
+
+    # ---- decode as the measurement protocol times it: 50 calls at the chosen
+    # split count, each after a 512 MiB flush write (outside its events), median
+    settle(lambda: decode(best_ns), args.settle / 5)
+    dec_ms = timed(lambda: decode(best_ns), 50, stream, flush_caches)
     dec_gbps = kv_bytes / (dec_ms * 1e-3) / 1e9
 
-    # ---- the dominant kernel alone: the fused prefill kernel on the same shapes.
-    # Q and K are rotated once beforehand, so each attn_fwd call below is exactly
-    # one launch of the attention kernel (no table or key-rotation launches).
+    # ---- the dominant kernel: the fused RoPE attention kernel of the headline
+    # call, timed by the library's event pair around its launch (the cached
+    # RoPE table and the key-rotation pass of each call are outside the pair),
+    # over max(steps, 50) production calls; median.
+    settle(prefill, args.settle / 5)
+    kern_all = kernel_times(prefill, max(args.steps, 50))
+    kern_ms = float(np.median(kern_all))
+    kern_tflops = pc.flops / (kern_ms * 1e-3) / 1e12
+    traffic = read_traffic(pc.io_bytes)
+    # the same kernel without RoPE on pre-rotated Q and K, for context
     qr, kr = q.clone(), k.clone()
     xa.rope_apply(qr, 0, pc.rope_base)
     xa.rope_apply(kr, 0, pc.rope_base)
     torch.cuda.synchronize()
-    kern_ms = timed(lambda: xa.attn_fwd(qr, kr, v, causal=True, scale=pc.scale, o=o, lse=lse),
-                    max(args.steps, 20), stream)
-    kern_tflops = pc.flops / (kern_ms * 1e-3) / 1e12
-    traffic = read_traffic(pc.io_bytes)
+    nr_ms = float(np.median(kernel_times(
+        lambda: xa.attn_fwd(qr, kr, v, causal=True, scale=pc.scale, o=o, lse=lse),
+        max(args.steps, 50))))
+    del qr, kr
 
     # ---- backward of the same prefill (next to the hot path, not in `value`):
     # attn_bwd with the forward's O and LSE and a resident upstream gradient.
@@ -498,10 +540,10 @@ def main():
     mk_ms = timed(masked, max(args.steps // 2, 10), stream)
     mk_tflops = pc.flops / (mk_ms * 1e-3) / 1e12
 
-    # ---- the other prefill workloads (the parity cases' shapes), one call each
-    # (GPU time: the host's launch cost is kept out), for context: a single
-    # fp32 head (fp32 VALU path), MHA at 1024 tokens without and with the
-    # causal mask, the Whisper-encoder shape
+    # ---- the other prefill workloads (the parity cases' shapes): the
+    # attention kernel's GPU time per call (library event pairs, median of
+    # max(steps, 50)), for a single fp32 head (fp32 VALU path), MHA at 1024
+    # tokens without and with the causal mask, the Whisper-encoder shape
     others = {}
     for c in (W.C1, W.C2N, W.C2C, W.C3):
         qo_, ko_, vo_ = (W.to_device(x) for x in W.prefill_inputs(c))
@@ -511,7 +553,7 @@ def main():
         def call(c=c, qo_=qo_, ko_=ko_, vo_=vo_, oo_=oo_, lo_=lo_):
             xa.attn_fwd(qo_, ko_, vo_, causal=c.causal, scale=c.scale, o=oo_, lse=lo_)
         settle(call, args.settle / 5)
-        c_ms = timed_queued(call, max(args.steps, 20), stream)
+        c_ms = float(np.median(kernel_times(call, max(args.steps, 50))))
         c_tf = c.flops / (c_ms * 1e-3) / 1e12
         others[c.name] = {"shape": f"B{c.B} Hq{c.Hq} Hkv{c.Hkv} S{c.Sq} D{c.D} {c.dtype}"
                                    f"{' causal' if c.causal else ''}",
@@ -544,16 +586,30 @@ def main():
             "settle": {"seconds": args.settle, "untimed_steps": n_settle,
                        "seconds_before_backward_chunked_masked": args.settle / 2},
         },
-        "prefill": {"ms": round(pre_ms, 4), "tflops": round(pre_tflops, 2),
+        "prefill": {"what": "whole attn_fwd call (key rotation + attention kernel; RoPE table "
+                            "cached), events on the call's stream, median of the timed steps",
+                    "ms": round(pre_ms, 4), "ms_mean": round(float(np.mean(pre_all)), 4),
+                    "tflops": round(pre_tflops, 2),
                     "frac_of_mfma_peak": round(pre_tflops / PEAK_BF16_TFLOPS, 4)},
-        "decode": {"ms": round(dec_ms, 4), "GBps": round(dec_gbps, 1),
+        "decode": {"what": f"attn_decode_splitkv (split + merge) at {best_ns} splits, 50 calls "
+                           f"each after a {FLUSH_BYTES >> 20} MiB flush write outside the "
+                           "events, median",
+                   "ms": round(dec_ms, 4), "GBps": round(dec_gbps, 1),
                    "frac_of_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),
-                   "kv_bytes": kv_bytes,
+                   "kv_bytes": kv_bytes, "ms_in_timed_steps": round(step_dec_ms, 4),
                    "ms_by_splits": {str(k_): round(v_, 4) for k_, v_ in split_ms.items()}},
-        "roofline": {"kernel": "fwd16_kernel<bf16,D=64,HPW=4,causal>", "bound": "mfma",
+        "roofline": {"kernel": KERNEL_LABEL, "bound": "mfma",
                      "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
-                     "launch_ms": round(kern_ms, 4), "traffic": traffic},
+                     "launch_ms": round(kern_ms, 4),
+                     "launch_ms_mean": round(float(np.mean(kern_all)), 4),
+                     "timing": "HIP events recorded by the library around the kernel launch on "
+                               "the call's stream (attn_profile session), median",
+                     "traffic": traffic,
+                     "no_rope_variant": {"kernel": KERNEL_LABEL_NOROPE,
+                                         "launch_ms": round(nr_ms, 4),
+                                         "frac": round(pc.flops / (nr_ms * 1e-3) / 1e12 /
+                                                       PEAK_BF16_TFLOPS, 4)}},
         "backward": {"workload": "LFM2 GQA prefill backward (dq, dk, dv), RoPE, causal",
                      "ms": round(bwd_ms, 4), "tflops": round(bwd_tflops, 2),
                      "frac_of_mfma_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),

@@ -14,6 +14,7 @@ Entry points (same names as the C ABI):
   attn_decode_splitkv(q, kcache, vcache, seqlens, num_splits, scale=None, ...)
   rope_apply(x, pos_offset=0, rope_base=10000.0)
   attn_decode_workspace_bytes(B, Hq, D, num_splits)
+  attn_profile_begin(), attn_profile_end() -> per-launch attention-kernel ms
 """
 import ctypes
 import math
@@ -26,8 +27,9 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_EMPTY_KV = 0, -1, -2, -3, -4
-EXPORTS = ("attn_fwd", "attn_fwd_masked", "attn_bwd_workspace_bytes", "attn_bwd", "attn_decode_workspace_bytes",
-           "attn_decode_splitkv", "attn_prefill_kvcache", "rope_apply", "attn_last_error")
+EXPORTS = ("attn_fwd", "attn_fwd_masked", "attn_bwd_workspace_bytes", "attn_bwd",
+           "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_prefill_kvcache",
+           "rope_apply", "attn_last_error", "attn_profile_begin", "attn_profile_end")
 
 _lib = None
 
@@ -69,6 +71,10 @@ def load():
     lib.rope_apply.restype = i
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_profile_begin.argtypes = []
+    lib.attn_profile_begin.restype = i
+    lib.attn_profile_end.argtypes = [ctypes.POINTER(ctypes.c_float), i, ctypes.POINTER(i)]
+    lib.attn_profile_end.restype = i
     _lib = lib
     return lib
 
@@ -102,11 +108,57 @@ def _stream(stream):
 
 
 def _need_gpu(*ts):
+    dev = None
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError("tensors must be on a GPU device")
-        if t is not None and not t.is_contiguous():
+        if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices ({dev} and {t.device})")
+
+
+def _check_out(t, name, shape, dtype):
+    """A caller-supplied output must have exactly the shape and dtype the
+    kernels write (they take only its pointer)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _mask_view(mask, B, Hq, Sq, Skv):
+    """The fp32 mask as a [B, Hq, Sq, Skv] view whose broadcast dimensions
+    have stride 0 and whose keys are contiguous (the C ABI takes strides for
+    batch, head and row only).  A mask broadcast over the keys (last dimension
+    1, or a 0-d mask) is first expanded to Skv columns in memory, keeping its
+    leading dimensions; a last dimension with another stride is copied."""
+    if mask.dtype != torch.float32:
+        raise TypeError("mask must be fp32")
+    if mask.dim() > 4:
+        raise ValueError("mask has more than 4 dimensions")
+    if mask.dim() == 0 or mask.shape[-1] != Skv:
+        lead = tuple(mask.shape[:-1]) if mask.dim() > 0 else ()
+        if mask.dim() > 0 and mask.shape[-1] != 1:
+            raise ValueError(f"mask {tuple(mask.shape)} does not broadcast to "
+                             f"[{B}, {Hq}, {Sq}, {Skv}]")
+        mask = mask.reshape(*lead, 1).expand(*lead, Skv).contiguous()
+    elif mask.stride(-1) != 1:
+        mask = mask.contiguous()
+    try:
+        m = mask.expand(B, Hq, Sq, Skv)
+    except RuntimeError as e:
+        raise ValueError(f"mask {tuple(mask.shape)} does not broadcast to "
+                         f"[{B}, {Hq}, {Sq}, {Skv}]") from e
+    if Skv > 1 and m.stride(3) != 1:
+        raise ValueError("mask keys must be contiguous")
+    return m
 
 
 def attn_fwd(q, k, v, causal=False, scale=None, rope_base=0.0, o=None, lse=None, stream=None,
@@ -121,6 +173,8 @@ def attn_fwd(q, k, v, causal=False, scale=None, rope_base=0.0, o=None, lse=None,
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
+    _check_out(o, "o", q.shape, q.dtype)
+    _check_out(lse, "lse", (B, Hq, Sq), torch.float32)
     if o is None:
         o = torch.empty_like(q)
     if lse is None and want_lse:
@@ -138,29 +192,23 @@ def attn_fwd_masked(q, k, v, mask, causal=False, scale=None, rope_base=0.0, o=No
     """attn_fwd with an additive fp32 mask added to the scaled scores.
 
     mask: fp32 tensor broadcastable to [B, Hq, Sq, Skv] (e.g. [Sq, Skv],
-    [B, 1, 1, Skv]); broadcast dimensions are passed as zero strides, so the
-    mask is never expanded in memory.  Its last dimension must be contiguous
-    (a mask whose last stride is not 1 is first made contiguous)."""
+    [B, 1, 1, Skv]); broadcast batch, head and row dimensions are passed as
+    zero strides, so they are never expanded in memory.  The kernels read a
+    row's keys at consecutive addresses: a mask whose last stride is not 1 is
+    first made contiguous, and one broadcast over the keys (last dimension 1,
+    or 0-d) is first expanded to Skv columns."""
     _need_gpu(q, k, v, o, lse)
-    if not mask.is_cuda:
-        raise ValueError("tensors must be on a GPU device")
+    if not mask.is_cuda or mask.device != q.device:
+        raise ValueError("mask must be on q's GPU device")
     B, Sq, Hq, D = q.shape
     Bk, Skv, Hkv, Dk = k.shape
     if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
-    if mask.dtype != torch.float32:
-        raise TypeError("mask must be fp32")
-    if mask.dim() > 4:
-        raise ValueError("mask has more than 4 dimensions")
-    if mask.dim() >= 1 and mask.shape[-1] > 1 and mask.stride(-1) != 1:
-        mask = mask.contiguous()
-    try:
-        m = mask.expand(B, Hq, Sq, Skv)
-    except RuntimeError as e:
-        raise ValueError(f"mask {tuple(mask.shape)} does not broadcast to "
-                         f"[{B}, {Hq}, {Sq}, {Skv}]") from e
+    m = _mask_view(mask, B, Hq, Sq, Skv)
+    _check_out(o, "o", q.shape, q.dtype)
+    _check_out(lse, "lse", (B, Hq, Sq), torch.float32)
     if o is None:
         o = torch.empty_like(q)
     if lse is None and want_lse:
@@ -198,6 +246,9 @@ def attn_bwd(q, k, v, o, dout, lse, causal=False, scale=None, rope_base=0.0, dq=
     if workspace is not None and workspace.numel() * workspace.element_size() < \
             attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, rope_base):
         raise ValueError("workspace smaller than attn_bwd_workspace_bytes")
+    _check_out(dq, "dq", q.shape, q.dtype)
+    _check_out(dk, "dk", k.shape, k.dtype)
+    _check_out(dv, "dv", v.shape, v.dtype)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -228,6 +279,8 @@ def attn_decode_splitkv(q, kcache, vcache, seqlens, num_splits, scale=None, o=No
         raise ValueError("seqlens must be int32 [B]")
     if q.dtype != torch.bfloat16 or kcache.dtype != torch.bfloat16 or vcache.dtype != torch.bfloat16:
         raise TypeError("decode takes bf16 q and caches")
+    _check_out(o, "o", q.shape, q.dtype)
+    _check_out(lse, "lse", (B, Hq), torch.float32)
     if o is None:
         o = torch.empty_like(q)
     if lse is None and want_lse:
@@ -260,6 +313,8 @@ def attn_prefill_kvcache(q, k_new, v_new, kcache, vcache, cache_lens, causal=Tru
         raise ValueError("cache_lens must be int32 [B]")
     if not (q.dtype == k_new.dtype == v_new.dtype == kcache.dtype == vcache.dtype == torch.bfloat16):
         raise TypeError("bf16 tensors expected")
+    _check_out(o, "o", q.shape, q.dtype)
+    _check_out(lse, "lse", (B, Hq, Sq), torch.float32)
     if o is None:
         o = torch.empty_like(q)
     if lse is None and want_lse:
@@ -280,3 +335,18 @@ def rope_apply(x, pos_offset=0, rope_base=10000.0, stream=None):
     _check(load().rope_apply(_ptr(x), B, S, H, D, int(pos_offset), float(rope_base),
                              _dtype_code(x), _stream(stream)))
     return x
+
+
+def attn_profile_begin():
+    """Start recording HIP events around the attention-kernel launch of every
+    later forward call (attn_fwd, attn_fwd_masked, attn_prefill_kvcache)."""
+    _check(load().attn_profile_begin())
+
+
+def attn_profile_end(cap=4096):
+    """Stop recording; returns the recorded launches' GPU times in ms, in
+    launch order (waits for them)."""
+    buf = (ctypes.c_float * max(cap, 0))()
+    n = ctypes.c_int(0)
+    _check(load().attn_profile_end(buf, int(cap), ctypes.byref(n)))
+    return [float(buf[i]) for i in range(min(n.value, cap))]

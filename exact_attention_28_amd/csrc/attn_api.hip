@@ -44,9 +44,15 @@ int ok() {
 }
 
 // Library-owned device buffers of one device: grow-only, kept until exit.
+// A buffer that a stream capture has referenced is "frozen": the captured
+// graph holds its address (and, for the RoPE table, replays a build into it),
+// so it is never freed and never trusted as a cache afterwards.  When such a
+// buffer must grow, or an eager call needs a table in it, the library moves
+// to a new allocation and keeps the old one alive in `retired` until exit.
 struct DevBuffers {
   void* rope_tab = nullptr;
   size_t rope_tab_bytes = 0;
+  bool rope_tab_frozen = false;
   // what the RoPE table holds: positions [tab_pos0, tab_pos0 + tab_npos) for
   // head dim tab_D and base tab_base, written on tab_stream
   bool tab_ok = false;
@@ -55,34 +61,111 @@ struct DevBuffers {
   hipStream_t tab_stream = nullptr;
   void* kstage = nullptr;
   size_t kstage_bytes = 0;
+  bool kstage_frozen = false;
   void* dec_ws = nullptr;
   size_t dec_ws_bytes = 0;
+  bool dec_ws_frozen = false;
   void* bwd_ws = nullptr;
   size_t bwd_ws_bytes = 0;
+  bool bwd_ws_frozen = false;
   void* pad_ws = nullptr;
   size_t pad_ws_bytes = 0;
+  bool pad_ws_frozen = false;
   void* split_ws = nullptr;  // key-split partials of under-filled forward launches
   size_t split_ws_bytes = 0;
+  bool split_ws_frozen = false;
+  std::vector<void*> retired;  // frozen buffers that were replaced; never freed
 };
 
 std::mutex g_mu;
 std::map<int, DevBuffers> g_dev;
 
-// Make *p hold at least `need` bytes on the current device.
-int grow(void** p, size_t* cap, size_t need, const char* what) {
-  if (*cap >= need && *p != nullptr) return ATTN_OK;
+// Kernel-timing session (attn_profile_begin / attn_profile_end): event pairs
+// recorded around the attention-kernel launches of forward calls.  Events
+// are created on demand and reused by later sessions.
+struct ProfEvents {
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfEvents> g_prof_pool;  // every event pair created so far
+size_t g_prof_used = 0;               // pairs recorded in this session
+
+// Whether `stream` is being captured into a graph (a query error counts as no).
+bool capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+    (void)hipGetLastError();  // not left for the launch checks that follow
+    return false;
+  }
+  return cap != hipStreamCaptureStatusNone;
+}
+
+// With a profiling session open and `stream` not capturing, the event pair
+// that brackets the next attention-kernel launch (nullptr otherwise).
+ProfEvents* prof_pair(hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  if (!g_prof_on || capturing(stream)) return nullptr;
+  if (g_prof_used == g_prof_pool.size()) {
+    ProfEvents pe;
+    if (hipEventCreate(&pe.start) != hipSuccess) return nullptr;
+    if (hipEventCreate(&pe.stop) != hipSuccess) {
+      (void)hipEventDestroy(pe.start);
+      return nullptr;
+    }
+    g_prof_pool.push_back(pe);
+  }
+  return &g_prof_pool[g_prof_used++];
+}
+
+// Launch `launch` (returning hipError_t) bracketed by a profiling event pair
+// when a session is open.
+template <typename F>
+hipError_t timed_launch(hipStream_t stream, F&& launch) {
+  ProfEvents* pe = prof_pair(stream);
+  if (pe != nullptr) {
+    hipError_t e = hipEventRecord(pe->start, stream);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (e == hipSuccess && pe != nullptr) e = hipEventRecord(pe->stop, stream);
+  return e;
+}
+
+// Make *p hold at least `need` bytes on the current device, for a call on
+// `stream`.  A buffer used while `stream` is captured becomes frozen; a frozen
+// buffer (or any buffer while capturing, where hipFree would have to
+// synchronise) is retired instead of freed when it has to grow.
+int grow(DevBuffers* db, void** p, size_t* cap, bool* frozen, size_t need, const char* what,
+         hipStream_t stream) {
+  const bool cap_now = capturing(stream);
+  if (*cap >= need && *p != nullptr) {
+    if (cap_now) *frozen = true;
+    return ATTN_OK;
+  }
   if (*p != nullptr) {
-    hipError_t e = hipFree(*p);  // synchronises the device before the buffer goes
+    if (*frozen || cap_now) {
+      db->retired.push_back(*p);
+    } else {
+      hipError_t e = hipFree(*p);  // synchronises the device before the buffer goes
+      if (e != hipSuccess) {
+        *p = nullptr;
+        *cap = 0;
+        return fail(ATTN_ERR_HIP, "hipFree(%s): %s", what, hipGetErrorString(e));
+      }
+    }
     *p = nullptr;
     *cap = 0;
-    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipFree(%s): %s", what, hipGetErrorString(e));
   }
   hipError_t e = hipMalloc(p, need);
   if (e != hipSuccess) {
     *p = nullptr;
-    return fail(ATTN_ERR_HIP, "hipMalloc(%s, %zu bytes): %s", what, need, hipGetErrorString(e));
+    return fail(ATTN_ERR_HIP, "hipMalloc(%s, %zu bytes)%s: %s", what, need,
+                cap_now ? " during stream capture (run the call once before capturing)" : "",
+                hipGetErrorString(e));
   }
   *cap = need;
+  *frozen = cap_now;
   return ATTN_OK;
 }
 
@@ -108,12 +191,7 @@ int debug_check_lens(const char* fn, const char* what, const int* lens, int B, i
                      hipStream_t stream) {
   const char* env = std::getenv("ATTN_DEBUG");
   if (env == nullptr || std::strcmp(env, "1") != 0) return ATTN_OK;
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
-    (void)hipGetLastError();
-    cap = hipStreamCaptureStatusNone;
-  }
-  if (cap != hipStreamCaptureStatusNone) return ATTN_OK;
+  if (capturing(stream)) return ATTN_OK;
   std::vector<int> h((size_t)B);
   hipError_t e = hipMemcpyAsync(h.data(), lens, (size_t)B * sizeof(int), hipMemcpyDeviceToHost,
                                 stream);
@@ -131,15 +209,15 @@ int debug_check_lens(const char* fn, const char* what, const int* lens, int B, i
 // cache capacity) and, when there are any, the library-owned partial buffer.
 // The caller holds g_mu.
 int plan_splits_locked(DevBuffers* db, int B, int Hq, int Hkv, int Sq, int kv_rows, int D,
-                       bool masked, xattn::KeySplit* ks) {
+                       bool masked, xattn::KeySplit* ks, hipStream_t stream) {
   *ks = xattn::KeySplit();
   if (masked) return ATTN_OK;
   const int n = xattn::fwd16_key_splits(B, Hq, Hkv, Sq, kv_rows, D);
   if (n <= 1) return ATTN_OK;
   const size_t rows = (size_t)B * Sq * Hq;
   const size_t obytes = (rows * n * D * 4 + 255) & ~(size_t)255;
-  int st = grow(&db->split_ws, &db->split_ws_bytes, xattn::fwd16_split_ws_bytes(B, Hq, Sq, D, n),
-                "key-split partials");
+  int st = grow(db, &db->split_ws, &db->split_ws_bytes, &db->split_ws_frozen,
+                xattn::fwd16_split_ws_bytes(B, Hq, Sq, D, n), "key-split partials", stream);
   if (st != ATTN_OK) return st;
   ks->n = n;
   ks->o = static_cast<float*>(db->split_ws);
@@ -148,14 +226,14 @@ int plan_splits_locked(DevBuffers* db, int B, int Hq, int Hkv, int Sq, int kv_ro
 }
 
 int plan_splits(int B, int Hq, int Hkv, int Sq, int kv_rows, int D, bool masked,
-                xattn::KeySplit* ks) {
+                xattn::KeySplit* ks, hipStream_t stream) {
   *ks = xattn::KeySplit();
   if (masked || xattn::fwd16_key_splits(B, Hq, Hkv, Sq, kv_rows, D) <= 1) return ATTN_OK;
   std::lock_guard<std::mutex> lock(g_mu);
   int st;
   DevBuffers* db = buffers(&st);
   if (!db) return st;
-  return plan_splits_locked(db, B, Hq, Hkv, Sq, kv_rows, D, masked, ks);
+  return plan_splits_locked(db, B, Hq, Hkv, Sq, kv_rows, D, masked, ks, stream);
 }
 
 int hip_status(hipError_t e, const char* what) {
@@ -169,29 +247,32 @@ int hip_status(hipError_t e, const char* what) {
 // are the same; stream order puts its build before this call's kernels);
 // otherwise the table is rebuilt on `stream`.  While `stream` is being
 // captured into a graph the build is always recorded (a replay must not
-// depend on what the buffer holds then) and the table is not marked as built
-// (the recorded build has not run yet).
+// depend on what the buffer holds then), the buffer is frozen and the cache is
+// dropped: replays rewrite that buffer at times the host does not see, so an
+// eager call afterwards builds its table in a new buffer.
 int rope_table(DevBuffers* db, int pos0, int npos, int D, float base, hipStream_t stream,
                const double2** tab, const char* fn) {
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
-    (void)hipGetLastError();  // not left for the launch checks that follow
-    cap = hipStreamCaptureStatusNone;
-  }
-  const bool capturing = cap != hipStreamCaptureStatusNone;
-  if (!capturing && db->tab_ok && db->tab_stream == stream && db->tab_pos0 == pos0 &&
+  const bool cap_now = capturing(stream);
+  if (!cap_now && db->tab_ok && db->tab_stream == stream && db->tab_pos0 == pos0 &&
       db->tab_D == D && db->tab_base == (double)base && db->tab_npos >= npos) {
     *tab = static_cast<const double2*>(db->rope_tab);
     return ATTN_OK;
   }
   db->tab_ok = false;
+  if (!cap_now && db->rope_tab_frozen && db->rope_tab != nullptr) {
+    db->retired.push_back(db->rope_tab);
+    db->rope_tab = nullptr;
+    db->rope_tab_bytes = 0;
+    db->rope_tab_frozen = false;
+  }
   const size_t bytes = (size_t)npos * (D / 2) * sizeof(double2);
-  int st = grow(&db->rope_tab, &db->rope_tab_bytes, bytes, "rope table");
+  int st = grow(db, &db->rope_tab, &db->rope_tab_bytes, &db->rope_tab_frozen, bytes, "rope table",
+                stream);
   if (st != ATTN_OK) return st;
   hipError_t e = xattn::launch_rope_table(static_cast<double2*>(db->rope_tab), pos0, npos, D,
                                           (double)base, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: rope table launch: %s", fn, hipGetErrorString(e));
-  db->tab_ok = !capturing;
+  db->tab_ok = !cap_now;
   db->tab_pos0 = pos0;
   db->tab_npos = npos;
   db->tab_D = D;
@@ -215,8 +296,8 @@ int fwd_padded(const void* q, const void* k, const void* v, void* o, float* lse,
   int st;
   DevBuffers* db = buffers(&st);
   if (!db) return st;
-  if ((st = grow(&db->pad_ws, &db->pad_ws_bytes, 2 * qb + 2 * kb, "padded head dim staging")) !=
-      ATTN_OK)
+  if ((st = grow(db, &db->pad_ws, &db->pad_ws_bytes, &db->pad_ws_frozen, 2 * qb + 2 * kb,
+                 "padded head dim staging", stream)) != ATTN_OK)
     return st;
   char* base = static_cast<char*>(db->pad_ws);
   void *qp = base, *kp = base + qb, *vp = base + qb + kb, *op = base + qb + 2 * kb;
@@ -228,7 +309,8 @@ int fwd_padded(const void* q, const void* k, const void* v, void* o, float* lse,
   const int dt = dtype;  // kernel format codes: 0 fp32, 1 bf16, 2 fp16
   xattn::KeySplit ks;
   if (dtype != ATTN_F32 &&
-      (st = plan_splits_locked(db, B, Hq, Hkv, Sq, Skv, Dp, mask.p != nullptr, &ks)) != ATTN_OK)
+      (st = plan_splits_locked(db, B, Hq, Hkv, Sq, Skv, Dp, mask.p != nullptr, &ks, stream)) !=
+          ATTN_OK)
     return st;
   if ((e = xattn::launch_pack_heads(q, qp, B, Sq, Hq, D, Dp, tab, Skv - Sq, dt, stream)) !=
           hipSuccess ||
@@ -236,12 +318,13 @@ int fwd_padded(const void* q, const void* k, const void* v, void* o, float* lse,
       (e = xattn::launch_pack_heads(v, vp, B, Skv, Hkv, D, Dp, nullptr, 0, dt, stream)) !=
           hipSuccess)
     return hip_status(e, "attn_fwd: head-dim padding launch");
-  if (dtype != ATTN_F32)
-    e = xattn::launch_fwd16(qp, kp, vp, op, lse, B, Hq, Hkv, Sq, Skv, Dp, causal, scale, nullptr,
-                            dt, stream, nullptr, 0, mask, ks);
-  else
-    e = xattn::launch_fwd_f32(qp, kp, vp, op, lse, B, Hq, Hkv, Sq, Skv, Dp, causal, scale,
-                              nullptr, stream, mask);
+  e = timed_launch(stream, [&] {
+    if (dtype != ATTN_F32)
+      return xattn::launch_fwd16(qp, kp, vp, op, lse, B, Hq, Hkv, Sq, Skv, Dp, causal, scale,
+                                 nullptr, dt, stream, nullptr, 0, mask, ks);
+    return xattn::launch_fwd_f32(qp, kp, vp, op, lse, B, Hq, Hkv, Sq, Skv, Dp, causal, scale,
+                                 nullptr, stream, mask);
+  });
   if (e != hipSuccess) return hip_status(e, "attn_fwd: kernel launch");
   e = xattn::launch_unpack_heads(op, o, (long long)B * Sq * Hq, D, Dp, dt, stream);
   return hip_status(e, "attn_fwd: head-dim unpadding launch");
@@ -295,7 +378,9 @@ int fwd(const char* fn, const void* q, const void* k, const void* v, void* o, fl
     if ((st = rope_table(db, 0, Skv, D, rope_base, stream, &tab, fn)) != ATTN_OK) return st;
     if (dtype != ATTN_F32) {
       const size_t kb = (size_t)B * Skv * Hkv * D * 2;
-      if ((st = grow(&db->kstage, &db->kstage_bytes, kb, "rotated K")) != ATTN_OK) return st;
+      if ((st = grow(db, &db->kstage, &db->kstage_bytes, &db->kstage_frozen, kb, "rotated K",
+                     stream)) != ATTN_OK)
+        return st;
       hipError_t e = xattn::launch_rope_rotate_qk(nullptr, nullptr, B, Sq, Hq, k, db->kstage, Skv,
                                                   Hkv, D, tab, dtype, stream);
       if (e != hipSuccess) return hip_status(e, "attn_fwd: K rotation launch");
@@ -305,12 +390,16 @@ int fwd(const char* fn, const void* q, const void* k, const void* v, void* o, fl
   hipError_t e;
   if (dtype != ATTN_F32) {
     xattn::KeySplit ks;
-    if (int st = plan_splits(B, Hq, Hkv, Sq, Skv, D, mask.p != nullptr, &ks)) return st;
-    e = xattn::launch_fwd16(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab, dtype,
-                            stream, nullptr, 0, mask, ks);
+    if (int st = plan_splits(B, Hq, Hkv, Sq, Skv, D, mask.p != nullptr, &ks, stream)) return st;
+    e = timed_launch(stream, [&] {
+      return xattn::launch_fwd16(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab,
+                                 dtype, stream, nullptr, 0, mask, ks);
+    });
   } else {
-    e = xattn::launch_fwd_f32(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab,
-                              stream, mask);
+    e = timed_launch(stream, [&] {
+      return xattn::launch_fwd_f32(q, kin, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, tab,
+                                   stream, mask);
+    });
   }
   return hip_status(e, "attn_fwd: kernel launch");
 }
@@ -320,6 +409,33 @@ int fwd(const char* fn, const void* q, const void* k, const void* v, void* o, fl
 extern "C" {
 
 const char* attn_last_error(void) { return g_err.c_str(); }
+
+int attn_profile_begin(void) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  g_prof_on = true;
+  g_prof_used = 0;
+  return ok();
+}
+
+int attn_profile_end(float* ms, int cap, int* n) {
+  if (n == nullptr || cap < 0) return fail(ATTN_ERR_INVALID, "attn_profile_end: null n or cap < 0");
+  if (cap > 0 && ms == nullptr) return fail(ATTN_ERR_INVALID, "attn_profile_end: null ms");
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  g_prof_on = false;
+  *n = (int)g_prof_used;
+  for (size_t i = 0; i < g_prof_used; ++i) {
+    hipError_t e = hipEventSynchronize(g_prof_pool[i].stop);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, g_prof_pool[i].start, g_prof_pool[i].stop);
+    if (e != hipSuccess) {
+      g_prof_used = 0;
+      return fail(ATTN_ERR_HIP, "attn_profile_end: event %zu: %s", i, hipGetErrorString(e));
+    }
+    if ((int)i < cap) ms[i] = t;
+  }
+  g_prof_used = 0;
+  return ok();
+}
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
              int Hkv, int Sq, int Skv, int D, int causal, float scale, float rope_base,
@@ -392,9 +508,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     return st;
   void* ws = workspace;
   if (ws == nullptr) {
-    if ((st = grow(&db->bwd_ws, &db->bwd_ws_bytes,
-                   xattn::bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, rope), "backward workspace")) !=
-        ATTN_OK)
+    if ((st = grow(db, &db->bwd_ws, &db->bwd_ws_bytes, &db->bwd_ws_frozen,
+                   xattn::bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, rope), "backward workspace",
+                   stream)) != ATTN_OK)
       return st;
     ws = db->bwd_ws;
   }
@@ -439,9 +555,9 @@ int attn_decode_splitkv(const void* q, const void* kcache, const void* vcache,
     int st;
     DevBuffers* db = buffers(&st);
     if (!db) return st;
-    if ((st = grow(&db->dec_ws, &db->dec_ws_bytes,
-                   xattn::decode_workspace_bytes(B, Hq, D, num_splits), "decode workspace")) !=
-        ATTN_OK)
+    if ((st = grow(db, &db->dec_ws, &db->dec_ws_bytes, &db->dec_ws_frozen,
+                   xattn::decode_workspace_bytes(B, Hq, D, num_splits), "decode workspace",
+                   stream)) != ATTN_OK)
       return st;
     ws = db->dec_ws;
   }
@@ -498,12 +614,15 @@ int attn_prefill_kvcache(const void* q, const void* k_new, const void* v_new, vo
   // every buffer is in place before the first launch, so a failure leaves the
   // caller's cache untouched
   xattn::KeySplit ks;
-  if (int st = plan_splits(B, Hq, Hkv, Sq, max_seqlen, D, false, &ks)) return st;
+  if (int st = plan_splits(B, Hq, Hkv, Sq, max_seqlen, D, false, &ks, stream)) return st;
   hipError_t e = xattn::launch_cache_append(k_new, v_new, kcache, vcache, cache_lens, B, Sq, Hkv,
                                             D, max_seqlen, tab, stream);
   if (e != hipSuccess) return hip_status(e, "attn_prefill_kvcache: append launch");
-  e = xattn::launch_fwd16(q, kcache, vcache, o, lse, B, Hq, Hkv, Sq, max_seqlen, D, causal, scale,
-                          tab, ATTN_BF16, stream, cache_lens, max_seqlen, xattn::MaskView(), ks);
+  e = timed_launch(stream, [&] {
+    return xattn::launch_fwd16(q, kcache, vcache, o, lse, B, Hq, Hkv, Sq, max_seqlen, D, causal,
+                               scale, tab, ATTN_BF16, stream, cache_lens, max_seqlen,
+                               xattn::MaskView(), ks);
+  });
   return hip_status(e, "attn_prefill_kvcache: kernel launch");
 }
 

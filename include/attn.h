@@ -38,8 +38,14 @@
  *  - HIP graph capture: a call can be captured once the library-owned buffers
  *    it uses are large enough (an earlier call of the same or a larger shape;
  *    or pass the workspaces explicitly), since capture cannot allocate.  A
- *    captured call records its RoPE table build; the library's buffers are
- *    shared, so replays must be ordered with other calls that use them.
+ *    captured call records its RoPE table build.  Every library buffer that a
+ *    capture references is kept alive until the process ends: when a later
+ *    call needs it larger, the library allocates a new one and retires the
+ *    old one instead of freeing it, so a graph never replays into freed
+ *    memory.  A replay rewrites its table buffer at times the host does not
+ *    see, so an eager call after a capture builds its table in a new buffer
+ *    rather than trusting the cache.  The library's buffers are shared, so
+ *    replays must still be ordered with other calls that use them.
  */
 #ifndef EXACT_ATTN_H
 #define EXACT_ATTN_H
@@ -289,6 +295,28 @@ int rope_apply(void* x, int B, int S, int H, int D, int pos_offset, float rope_b
 
 /* Text of the last error raised on the calling thread ("" if none). */
 const char* attn_last_error(void);
+
+/*
+ * Kernel timing (tracing; not part of the method).  A forward call launches
+ * up to three kernels (the RoPE table build, the key rotation, the attention
+ * kernel); a caller's events around the call time all of them.  Between
+ * attn_profile_begin() and attn_profile_end(), every attn_fwd,
+ * attn_fwd_masked and attn_prefill_kvcache call records a pair of HIP events
+ * on its own stream immediately before and after the launch of its attention
+ * kernel (with the key-split merge when the keys are split), so their
+ * difference is that kernel's GPU time.  Calls on a stream being captured
+ * into a graph record nothing.
+ *   attn_profile_begin: starts a session (drops one still open).  Returns
+ *     ATTN_OK, or ATTN_ERR_HIP if events cannot be created later.
+ *   attn_profile_end: waits for the recorded events, writes up to `cap`
+ *     per-launch times in milliseconds, in launch order, to ms (may be NULL
+ *     when cap is 0) and the number of launches recorded to *n, and ends the
+ *     session.  ATTN_ERR_INVALID for a null n or cap < 0; ATTN_ERR_HIP if an
+ *     event query fails.
+ * The session is process-wide (one at a time); the events are the library's.
+ */
+int attn_profile_begin(void);
+int attn_profile_end(float* ms, int cap, int* n);
 
 #ifdef __cplusplus
 }

@@ -57,6 +57,11 @@
 
 /* ---------------------------------------------------------------- inputs -- */
 
+/* the input formats widen() reads; any other code is rejected by the entry points */
+static int known_dtype(int dtype) {
+  return dtype == ORC_F64 || dtype == ORC_F32 || dtype == ORC_BF16 || dtype == ORC_F16;
+}
+
 static double widen(const void* p, int dtype, size_t idx) {
   if (dtype == ORC_F64) return ((const double*)p)[idx];
   if (dtype == ORC_F32) return (double)((const float*)p)[idx];
@@ -128,6 +133,7 @@ static void rope_rotate(double* x, int D, double pos, double base) {
 int oracle_rope(const void* x, int dtype, double* out, int B, int S, int H, int D,
                 int pos_offset, double base, int round_bits) {
   if (D % 2 != 0) return -1; /* [GQA] RoPE head_dim must be even */
+  if (!known_dtype(dtype)) return -1;
   double* row = (double*)malloc(sizeof(double) * (size_t)D);
   if (!row) return -2;
   for (int b = 0; b < B; ++b)
@@ -292,6 +298,7 @@ int oracle_attn_fwd(const void* q, const void* k, const void* v, int dtype, int 
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1) return -1;
   if (Hq % Hkv != 0) return -1;
   if (rope_base > 0.0 && D % 2 != 0) return -1;
+  if (!known_dtype(dtype)) return -1;
   if (nthreads < 1) nthreads = 1;
   fwd_job* jobs = (fwd_job*)calloc((size_t)nthreads, sizeof(fwd_job));
   pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
@@ -373,6 +380,7 @@ int oracle_decode(const void* q, const void* kc, const void* vc, int dtype, cons
                   int B, int Hq, int Hkv, int D, int Smax, double scale, const int* units,
                   int nunits, double* o, double* lse, int nthreads) {
   if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || Smax < 1 || Hq % Hkv != 0) return -1;
+  if (!known_dtype(dtype)) return -1;
   for (int b = 0; b < B; ++b)
     if (seqlens[b] < 0 || seqlens[b] > Smax) return -1;
   if (nthreads < 1) nthreads = 1;
@@ -577,6 +585,7 @@ int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1) return -1;
   if (Hq % Hkv != 0) return -1;
   if (rope_base > 0.0 && D % 2 != 0) return -1;
+  if (!known_dtype(dtype)) return -1;
   if (nthreads < 1) nthreads = 1;
   bwd_job* jobs = (bwd_job*)calloc((size_t)nthreads, sizeof(bwd_job));
   pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));

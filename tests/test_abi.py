@@ -105,6 +105,56 @@ def test_attn_fwd_masked_binding_checks():
         xa.attn_fwd_masked(q, q, q, torch.zeros(4, 4))
 
 
+@pytest.mark.parametrize("shape", [(), (1,), (5, 1), (2, 1, 5, 1), (1, 3, 1, 1)])
+def test_mask_broadcast_over_keys_is_expanded(shape):
+    """A mask broadcast over the keys reaches the ABI with unit key stride
+    (the kernels read mask[row * rs + j] for j < Skv), with its values
+    repeated along the keys and its other broadcast dimensions still stride 0."""
+    import torch
+    B, Hq, Sq, Skv = 2, 3, 5, 7
+    mask = torch.arange(int(torch.tensor(shape).prod()) if shape else 1,
+                        dtype=torch.float32).reshape(shape)
+    m = xa._mask_view(mask, B, Hq, Sq, Skv)
+    assert tuple(m.shape) == (B, Hq, Sq, Skv)
+    assert m.stride(3) == 1
+    ref = mask.expand(B, Hq, Sq, Skv)
+    # what the kernels read through the three strides and unit key stride
+    flat = m.as_strided((m.untyped_storage().nbytes() // 4,), (1,), 0)
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(Sq):
+                base = m.storage_offset() + b * m.stride(0) + h * m.stride(1) + i * m.stride(2)
+                assert torch.equal(flat[base:base + Skv], ref[b, h, i])
+
+
+def test_mask_view_keeps_zero_strides_and_rejects_bad_shapes():
+    import torch
+    m = xa._mask_view(torch.zeros(5, 7), 2, 3, 5, 7)
+    assert m.stride() == (0, 0, 7, 1)
+    m = xa._mask_view(torch.zeros(2, 1, 1, 7), 2, 3, 5, 7)
+    assert m.stride()[1:] == (0, 0, 1)
+    t = torch.zeros(7, 5).t()  # keys not contiguous: copied
+    assert xa._mask_view(t, 2, 3, 5, 7).stride(3) == 1
+    with pytest.raises(ValueError):
+        xa._mask_view(torch.zeros(5, 6), 2, 3, 5, 7)
+    with pytest.raises(ValueError):
+        xa._mask_view(torch.zeros(4, 7), 2, 3, 5, 7)
+    with pytest.raises(TypeError):
+        xa._mask_view(torch.zeros(5, 7, dtype=torch.float16), 2, 3, 5, 7)
+
+
+def test_output_checks():
+    """Caller-supplied outputs whose shape or dtype differs from what the
+    kernels write are refused (the ABI takes only their pointers)."""
+    import torch
+    xa._check_out(None, "o", (2, 3), torch.float32)
+    xa._check_out(torch.zeros(2, 3), "o", (2, 3), torch.float32)
+    with pytest.raises(ValueError):
+        xa._check_out(torch.zeros(2, 2), "o", (2, 3), torch.float32)
+    with pytest.raises(TypeError):
+        xa._check_out(torch.zeros(2, 3, dtype=torch.float16), "lse", (2, 3), torch.float32)
+
+
 def _dec(lib, q=FAKE, kc=FAKE, vc=FAKE, sl=FAKE, o=FAKE, B=2, Hq=8, Hkv=2, D=128, ns=4,
          scale=0.088, smax=64):
     return lib.attn_decode_splitkv(q, kc, vc, sl, o, B, Hq, Hkv, D, ns, scale, smax, None, None,
@@ -208,3 +258,14 @@ def _pkv(lib, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, o=FAKE, B=2
 def test_prefill_kvcache_validation(lib, kw, code):
     assert _pkv(lib, **kw) == code
     assert xa.last_error() != ""
+
+
+def test_profile_session_validation(lib):
+    """The kernel-timing session's host-side checks (no forward call in
+    between, so no event is created)."""
+    assert lib.attn_profile_end(None, 0, None) == xa.ATTN_ERR_INVALID
+    n = ctypes.c_int(7)
+    assert lib.attn_profile_end(None, -1, ctypes.byref(n)) == xa.ATTN_ERR_INVALID
+    assert lib.attn_profile_end(None, 3, ctypes.byref(n)) == xa.ATTN_ERR_INVALID
+    assert lib.attn_profile_begin() == xa.ATTN_OK
+    assert lib.attn_profile_end(None, 0, ctypes.byref(n)) == xa.ATTN_OK and n.value == 0

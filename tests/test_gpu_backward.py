@@ -116,24 +116,29 @@ def test_bwd_mha_1024_workload_full():
         check_grad(g, r, f"{cfg.name} {n}")
 
 
-def test_bwd_lfm2_workload_one_group():
+def test_bwd_lfm2_workload_four_groups():
     """The LFM2 prefill workload at full size (B4 Hq32 Hkv8 S4096 causal RoPE),
-    in the launch configuration the benchmark times; the oracle evaluates one
-    (batch, kv head) with its 4 query heads: dk, dv of that kv head and dq of
-    those heads, every element."""
+    in the launch configuration the benchmark times; the oracle evaluates four
+    (batch, kv head) units, the first and last batch with the first and last
+    kv head, each with its 4 query heads: dk, dv of those kv heads and dq of
+    their query heads, every element."""
     cfg = W.C4
     say("case", cfg.name, "backward")
     q, k, v = W.prefill_inputs(cfg)
     rng = np.random.default_rng(cfg.seed + 7)
     do = W.f32_to_bf16_bits(rng.standard_normal(q.shape, dtype=np.float32))
     dq, dk, dv = run_bwd(q, k, v, do, cfg.causal, cfg.scale, cfg.rope_base)
-    b, g = 3, 5
     G = cfg.Hq // cfg.Hkv
+    pairs = [(0, 0), (0, cfg.Hkv - 1), (cfg.B - 1, 0), (cfg.B - 1, cfg.Hkv - 1)]
     rq, rk, rv = oracle.attn_bwd(q, k, v, do, causal=cfg.causal, scale=cfg.scale,
-                                 rope_base=cfg.rope_base, units=[b * cfg.Hkv + g], nthreads=1)
-    check_grad(dq[b, :, g * G:(g + 1) * G], rq[b, :, g * G:(g + 1) * G], f"{cfg.name} dq")
-    check_grad(dk[b, :, g], rk[b, :, g], f"{cfg.name} dk")
-    check_grad(dv[b, :, g], rv[b, :, g], f"{cfg.name} dv")
+                                 rope_base=cfg.rope_base, units=[b * cfg.Hkv + g for b, g in pairs],
+                                 nthreads=min(4, NTHREADS))
+    for b, g in pairs:
+        say(f"  unit b={b} kv head {g}")
+        check_grad(dq[b, :, g * G:(g + 1) * G], rq[b, :, g * G:(g + 1) * G],
+                   f"{cfg.name} dq b{b} g{g}")
+        check_grad(dk[b, :, g], rk[b, :, g], f"{cfg.name} dk b{b} g{g}")
+        check_grad(dv[b, :, g], rv[b, :, g], f"{cfg.name} dv b{b} g{g}")
 
 
 def test_bwd_deterministic_and_workspace():

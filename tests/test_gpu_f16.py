@@ -102,9 +102,9 @@ def test_f16_masked(Skv):
     check_f16(_np(o), _np(lse), o_ref, lse_ref, "f16 masked")
 
 
-def test_f16_lfm2_workload_sampled():
+def test_f16_lfm2_workload_full():
     """The LFM2 prefill shape (B4 Hq32 Hkv8 S4096 D64 causal RoPE) with the
-    workload's fp32 draws rounded to fp16 instead of bf16, sampled rows of
+    workload's fp32 draws rounded to fp16 instead of bf16, every element of
     every (batch, head)."""
     cfg = W.C4
     say("case", cfg.name, "fp16")
@@ -116,14 +116,9 @@ def test_f16_lfm2_workload_sampled():
                          scale=cfg.scale, rope_base=cfg.rope_base)
     torch.cuda.synchronize()
     o, lse = _np(o), _np(lse)
-    rows = sorted(set([0, 1, 63, 64, 127, 128, cfg.Sq - 1] +
-                      [int(r) for r in rng.choice(cfg.Sq, 20, replace=False)]))
     o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal=True, scale=cfg.scale,
-                                     rope_base=cfg.rope_base, rows=rows,
-                                     units=list(range(cfg.B * cfg.Hq)), nthreads=NTHREADS)
-    og = o[:, rows].transpose(0, 2, 1, 3).reshape(cfg.B * cfg.Hq, len(rows), cfg.D)
-    lg = lse[:, :, rows].reshape(cfg.B * cfg.Hq, len(rows))
-    check_f16(og, lg, o_ref, lse_ref, f"{cfg.name} fp16")
+                                     rope_base=cfg.rope_base, nthreads=NTHREADS)
+    check_f16(o, lse, o_ref, lse_ref, f"{cfg.name} fp16")
 
 
 @pytest.mark.parametrize("D,off", [(64, 0), (128, 1000), (6, 3)])

@@ -168,10 +168,10 @@ def test_fully_hidden_rows_and_strided_mask():
     assert torch.equal(la, lb) and torch.equal(la, lc)
 
 
-def test_lfm2_workload_with_mask_sampled():
+def test_lfm2_workload_with_mask_full():
     """The LFM2 prefill workload (B4 Hq32 Hkv8 S4096 D64, causal, RoPE) with a
     shared [4096, 4096] mask (a 1024-key sliding window plus random -inf and
-    normal entries inside it), sampled rows of every (batch, head)."""
+    normal entries inside it), every element of every (batch, head)."""
     cfg = W.C4
     say("case", cfg.name, "masked")
     q, k, v = W.prefill_inputs(cfg)
@@ -181,14 +181,9 @@ def test_lfm2_workload_with_mask_sampled():
     i, j = np.arange(S)[:, None], np.arange(S)[None, :]
     mask[j < i - 1023] = -np.inf
     o, lse = run_masked(q, k, v, mask, cfg.causal, cfg.scale, cfg.rope_base)
-    rows = sorted(set([0, 1, 63, 64, 1023, 1024, 1025, S - 1] +
-                      [int(r) for r in rng.choice(S, 24, replace=False)]))
     o_ref, lse_ref = _oracle(q, k, v, mask, cfg.causal, cfg.scale, cfg.rope_base, cfg.B, cfg.Hq,
-                             S, S, rows=rows, units=list(range(cfg.B * cfg.Hq)))
-    # o: [B,Sq,Hq,D] -> [unit, row, D];  lse: [B,Hq,Sq] -> [unit, row]
-    og = o[:, rows].transpose(0, 2, 1, 3).reshape(cfg.B * cfg.Hq, len(rows), cfg.D)
-    lg = lse[:, :, rows].reshape(cfg.B * cfg.Hq, len(rows))
-    check_bf16(og, lg, o_ref, lse_ref, f"{cfg.name} masked")
+                             S, S)
+    check_bf16(o, lse, o_ref, lse_ref, f"{cfg.name} masked")
 
 
 def test_mask_between_nan_guards():

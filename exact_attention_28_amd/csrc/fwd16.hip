@@ -70,35 +70,6 @@
 
 namespace xattn {
 
-// Chunk swizzles (16-byte chunks, XORed with a function of the row).  LDS has
-// 64 four-byte banks, i.e. 16 groups of one chunk.  K fragments are read 16 rows
-// at a time at one logical chunk: the 16 (row, chunk) must fall in 16 distinct
-// groups.  V fragments are read by transpose reads covering 4 consecutive rows
-// (a multiple of 4 first) x 2 adjacent chunks (an even first): 8 distinct groups.
-template <int D>
-__device__ __forceinline__ int kswz(int row) {
-  return (D == 64) ? ((row >> 1) & 7) : (row & 15);  // group = (row*KCH + chunk) mod 16
-}
-template <int D>
-__device__ __forceinline__ int vswz(int row) {
-  return (D == 64) ? (2 * ((row >> 1) & 3)) : (2 * (row & 3));
-}
-
-// Direct HBM->LDS loads of one wave's share of a K and a V tile: instruction i
-// fills the 64 consecutive 16-byte slots starting at kdst/vdst + 1 KiB * i.
-// (A plain device function: the gfx950 LDS-load builtin cannot sit in a lambda,
-// which is also compiled for the host.)
-template <int LD>
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                         u16* kdst, u16* vdst, const uint32_t* koff,
-                                         const uint32_t* voff, uint32_t t0) {
-#pragma unroll
-  for (int i = 0; i < LD; ++i) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_ptr(kdst + i * 64 * 8), 16, koff[i] + t0, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_ptr(vdst + i * 64 * 8), 16, voff[i] + t0, 0, 0, 0);
-  }
-}
-
 // The shared-mask variant with 4 or 8 heads per workgroup needs 40-48 KiB of
 // LDS, so three workgroups fit a CU if the registers allow three waves per
 // SIMD (<= 168 VGPRs, reached without spills; measured 6 % faster).
@@ -765,6 +736,9 @@ hipError_t launch_fwd16(const void* q, const void* k, const void* v, void* o, fl
                         int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
                         const double2* rope_tab, int dtype, hipStream_t stream,
                         const int* kv_lens, int kv_rows, MaskView mask, KeySplit ks) {
+  if (mask.p == nullptr && ks.n <= 1 && fwd16_pipelined_enabled())
+    return launch_fwd16_pipelined(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale,
+                                  rope_tab, dtype, stream, kv_lens, kv_rows);
   if (kv_lens == nullptr) kv_rows = Skv;
   if (dtype == 1)
     return launch_fmt<__bf16>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, rope_tab,

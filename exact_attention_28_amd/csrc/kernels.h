@@ -49,6 +49,16 @@ hipError_t launch_fwd16(const void* q, const void* k, const void* v, void* o, fl
                         const int* kv_lens = nullptr, int kv_rows = 0,
                         MaskView mask = MaskView(), KeySplit ks = KeySplit());
 
+// The unmasked, unsplit 16-bit forward with the software-pipelined key loop
+// (fwd16p.hip): same arguments and results as launch_fwd16 without a mask or
+// key splits.  ATTN_FWD_PIPELINE=0 in the environment turns it off
+// (launch_fwd16 then runs fwd16_kernel for those launches too).
+bool fwd16_pipelined_enabled();
+hipError_t launch_fwd16_pipelined(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                                  int causal, float scale, const double2* rope_tab, int dtype,
+                                  hipStream_t stream, const int* kv_lens, int kv_rows);
+
 // Cache append: rows t < Sq of k_new/v_new [B,Sq,Hkv,D] (bf16) go to rows
 // L_b + t of kcache/vcache [B,rows,Hkv,D] with L_b = min(max(lens[b], 0),
 // rows - Sq); keys are rotated at position L_b + t (table row L_b + t, fp64,

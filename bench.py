@@ -9,13 +9,20 @@ One step is one pass of the whole path on resident synthetic inputs:
     pass and LSE merge — at the split count that measured fastest among
     4, 8, 16, 32, 64 before the timed region.
 
-Printed: one JSON line.  `value` is the prefill throughput in TFLOP/s
-(algorithmic flops 4*B*Hq*S*S*D/2 over the median event-timed attn_fwd call
-of the timed steps); the decode KV-read bandwidth (median of 50 calls, each
-after a 512 MiB flush write) and both fractions of peak sit beside it.  The
-`roofline` object is for the dominant kernel, the fused RoPE attention
-kernel of the headline call, timed by HIP events that the library records
-on the call's stream around that kernel's launch (attn_profile_begin/_end).
+Printed: one JSON line.  The timed region runs the K steps' work as K
+prefill calls back to back, then K decode calls, with a HIP event at each of
+the three boundaries only: every event recorded between two kernels costs
+the GPU a few microseconds of idle time (a kernel trace shows ~4 us per
+event on MI355X, ~5 us with the default system-scope fence), so no event
+sits inside either run.  `value` is the prefill throughput in TFLOP/s
+(algorithmic flops 4*B*Hq*S*S*D/2 over the mean attn_fwd call of the timed
+prefill run: key rotation + attention kernel); the decode KV-read bandwidth
+(median of 50 calls, each after a 512 MiB flush write) and both fractions of
+peak sit beside it.  The `roofline` object is for the dominant kernel, the
+fused RoPE attention kernel of the headline call, timed by the HIP event
+pair that the library attaches to that kernel's dispatch
+(attn_profile_begin/_end).  bench.py's own events are created without the
+system-scope fence (hipEventDisableSystemFence), which only timing needs.
 
 Modes for rocprofv3 runs (each launches one thing only): --profile-kernel
 REPS [--profile-workload NAME] (production attn_fwd calls on a prefill
@@ -44,13 +51,14 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 METRIC = "attention fwd TFLOP/s + decode KV GB/s, as % of MI355X MFMA/HBM peak"
-KERNEL_SOURCES = ("fwd16.hip", "common.h", "lds.h")
-# the attention kernel of the headline LFM2 prefill call (template arguments:
-# element type, head dim, query heads per workgroup, causal, fused query RoPE,
-# query blocks per wave, mask kind, key split)
-KERNEL_LABEL = "fwd16_kernel<__bf16, D=64, HPW=4, CAUSAL=1, ROPE=1, NQB=2, MASK=0, SPLIT=0>"
-KERNEL_LABEL_NOROPE = "fwd16_kernel<__bf16, D=64, HPW=4, CAUSAL=1, ROPE=0, NQB=2, MASK=0, SPLIT=0>"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd16_lfm2_gqa_prefill_s4096_traffic.txt")
+KERNEL_SOURCES = ("fwd16p.hip", "common.h", "lds.h")
+# the attention kernel of the headline LFM2 prefill call: the software-pipelined
+# kernel of unmasked, unsplit launches (template arguments: element type, head
+# dim, query heads per workgroup, causal, fused query RoPE, query blocks per wave)
+KERNEL_NAME = "fwdp_kernel"
+KERNEL_LABEL = "fwdp_kernel<__bf16, D=64, HPW=4, CAUSAL=1, ROPE=1, NQB=2>"
+KERNEL_LABEL_NOROPE = "fwdp_kernel<__bf16, D=64, HPW=4, CAUSAL=1, ROPE=0, NQB=2>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwdp_lfm2_gqa_prefill_s4096_traffic.txt")
 
 
 def log(*a):
@@ -94,8 +102,8 @@ def timed(fn, reps, stream, between=None):
     """Median duration (ms) of fn() over reps, each bracketed by HIP events on
     stream; `between` (e.g. a cache flush) runs before each repetition,
     outside the events."""
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    starts = [HipEvent() for _ in range(reps)]
+    ends = [HipEvent() for _ in range(reps)]
     for i in range(reps):
         if between is not None:
             between()
@@ -106,11 +114,45 @@ def timed(fn, reps, stream, between=None):
     return float(np.median([s.elapsed_time(e) for s, e in zip(starts, ends)]))
 
 
+class HipEvent:
+    """A HIP timing event without the system-scope fence of torch's events
+    (hipEventCreateWithFlags(hipEventDisableSystemFence)): reaching it does
+    not write back and invalidate the caches, which leaves less idle time
+    before the next kernel."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            HipEvent._hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch loaded
+        self._c = ctypes
+        self.h = ctypes.c_void_p()
+        rc = HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.h), ctypes.c_uint(0x20000000))
+        assert rc == 0, f"hipEventCreateWithFlags: {rc}"
+
+    def record(self, stream):
+        rc = HipEvent._hip.hipEventRecord(self.h, self._c.c_void_p(stream.cuda_stream))
+        assert rc == 0, f"hipEventRecord: {rc}"
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (waits for `end`)."""
+        rc = HipEvent._hip.hipEventSynchronize(end.h)
+        assert rc == 0, f"hipEventSynchronize: {rc}"
+        t = self._c.c_float()
+        rc = HipEvent._hip.hipEventElapsedTime(self._c.byref(t), self.h, end.h)
+        assert rc == 0, f"hipEventElapsedTime: {rc}"
+        return t.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.h:
+            HipEvent._hip.hipEventDestroy(self.h)
+
+
 def kernel_times(fn, reps):
     """Per-launch GPU times (ms) of the attention kernel of `reps` forward
-    calls fn(), from the library's event pairs around that launch (the
-    attn_profile session of the C ABI): the RoPE table build and key rotation
-    of a call are outside them."""
+    calls fn(), from the event pair that the library attaches to that
+    kernel's dispatch (the attn_profile session of the C ABI): the RoPE table
+    build and key rotation of a call are outside them."""
     xa.attn_profile_begin()
     for _ in range(reps):
         fn()
@@ -280,7 +322,7 @@ def counters_summary(csv_path, match, out_path, title, cmds):
     lines = [f"# {title}", "# Per-dispatch means over the matching dispatches "
              f"(kernel name containing '{match}').", "# Commands (from the repository root, "
              "TMPDIR=/tmp):", *[f"#   {c}" for c in cmds]]
-    if match.startswith("fwd16"):
+    if match.startswith(KERNEL_NAME):
         lines.append(f"kernel_source_sha256_16: {kernel_hash()}")
     for cn in sorted(vals):
         lines.append(f"{cn}: {np.mean(vals[cn]):.6g}  (dispatches: {len(vals[cn])})")
@@ -311,7 +353,7 @@ def traffic_summary(fetch_csv, write_csv, out_path, cmds):
                 continue
             name = r["Kernel_Name"]
             is_copy = "elementwise" in name and "add" in name.lower()  # not the fill of src
-            key = "attn" if "fwd16_kernel" in name else ("copy" if is_copy else None)
+            key = "attn" if KERNEL_NAME in name else ("copy" if is_copy else None)
             if key:
                 vals[key].append(float(r["Counter_Value"]))
         return {k_: float(np.mean(v_)) for k_, v_ in vals.items() if v_}
@@ -441,21 +483,23 @@ def main():
     best_ns = min(split_ms, key=split_ms.get)
     log("decode ms per split count:", {k_: round(v_, 4) for k_, v_ in split_ms.items()})
 
-    # ---- timed region: exactly `steps` steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # ---- timed region: exactly `steps` steps' work, as `steps` prefill calls
+    # back to back, then `steps` decode calls, events at the three boundaries
+    ev = [HipEvent() for _ in range(3)]
+    settle(prefill, args.settle / 5)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev[0].record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
         prefill()
-        ev[i][1].record(stream)
+    ev[1].record(stream)
+    for i in range(args.steps):
         decode(best_ns)
-        ev[i][2].record(stream)
+    ev[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_all = [e[0].elapsed_time(e[1]) for e in ev]
-    pre_ms = float(np.median(pre_all))
-    step_dec_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+    pre_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    step_dec_ms = ev[1].elapsed_time(ev[2]) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     pre_tflops = pc.flops / (pre_ms * 1e-3) / 1e12
 
@@ -587,8 +631,9 @@ def main():
                        "seconds_before_backward_chunked_masked": args.settle / 2},
         },
         "prefill": {"what": "whole attn_fwd call (key rotation + attention kernel; RoPE table "
-                            "cached), events on the call's stream, median of the timed steps",
-                    "ms": round(pre_ms, 4), "ms_mean": round(float(np.mean(pre_all)), 4),
+                            "cached): the timed region's prefill run of `steps` calls between "
+                            "two events, per call",
+                    "ms": round(pre_ms, 4),
                     "tflops": round(pre_tflops, 2),
                     "frac_of_mfma_peak": round(pre_tflops / PEAK_BF16_TFLOPS, 4)},
         "decode": {"what": f"attn_decode_splitkv (split + merge) at {best_ns} splits, 50 calls "
@@ -596,15 +641,19 @@ def main():
                            "events, median",
                    "ms": round(dec_ms, 4), "GBps": round(dec_gbps, 1),
                    "frac_of_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),
-                   "kv_bytes": kv_bytes, "ms_in_timed_steps": round(step_dec_ms, 4),
+                   "kv_bytes": kv_bytes,
+                   "ms_in_timed_region": round(step_dec_ms, 4),
+                   "ms_in_timed_region_what": "the timed region's decode run of `steps` calls "
+                                              "back to back (no flush) between two events, "
+                                              "per call",
                    "ms_by_splits": {str(k_): round(v_, 4) for k_, v_ in split_ms.items()}},
         "roofline": {"kernel": KERNEL_LABEL, "bound": "mfma",
                      "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
                      "launch_ms": round(kern_ms, 4),
                      "launch_ms_mean": round(float(np.mean(kern_all)), 4),
-                     "timing": "HIP events recorded by the library around the kernel launch on "
-                               "the call's stream (attn_profile session), median",
+                     "timing": "HIP event pair attached by the library to the kernel's dispatch "
+                               "(hipExtLaunchKernel; attn_profile session), median",
                      "traffic": traffic,
                      "no_rope_variant": {"kernel": KERNEL_LABEL_NOROPE,
                                          "launch_ms": round(nr_ms, 4),

@@ -631,18 +631,18 @@ static hipError_t go16(const void* q, const void* k, const void* v, void* o, flo
   const int nsplit = SPLIT ? ks.n : 1;
   const long long nblocks = (long long)n_qt * n_bh * nsplit;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  fwd16_kernel<T, D, HPW, CAUSAL, ROPE, NQB, MASK, SPLIT>
-      <<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
-          static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v),
-          static_cast<u16*>(o), lse, Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale * kLog2e, tab,
-          n_qt, n_bh, mask, scale, ks);
+  launch_kernel(fwd16_kernel<T, D, HPW, CAUSAL, ROPE, NQB, MASK, SPLIT>,
+                dim3((unsigned)nblocks), dim3(256), stream, static_cast<const u16*>(q),
+                static_cast<const u16*>(k), static_cast<const u16*>(v), static_cast<u16*>(o), lse,
+                Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale * kLog2e, tab, n_qt, n_bh, mask, scale,
+                ks);
   if constexpr (SPLIT) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long rows = (long long)B * Sq * Hq;
     constexpr int RPB = 256 / (D / 4);  // rows per block
-    fwd16_combine_kernel<T, D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream>>>(
-        ks.o, ks.l, static_cast<u16*>(o), lse, rows, Sq, Hq, nsplit);
+    launch_kernel(fwd16_combine_kernel<T, D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+                  stream, ks.o, ks.l, static_cast<u16*>(o), lse, rows, Sq, Hq, nsplit);
   }
   return hipGetLastError();
 }

@@ -81,6 +81,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   __shared__ __attribute__((aligned(16))) u16 Vs0[BN * D];
   __shared__ __attribute__((aligned(16))) u16 Ks1[BN * D];
   __shared__ __attribute__((aligned(16))) u16 Vs1[BN * D];
+  // RoPE (cos, sin) rows of the workgroup's NP positions, loaded once and
+  // read by every wave (the HPW heads of a position share its row) when the
+  // workgroup's LDS stays within 80 KiB (two workgroups per CU); otherwise
+  // each lane reads its rows from the table
+  constexpr bool TAB_LDS = ROPE && HPW > 1 && 4 * BN * D * 2 + NP * D * 8 <= 81920 &&
+                           (NP * D / 2) % 256 == 0;
+  __shared__ __attribute__((aligned(16))) double2 Ts[TAB_LDS ? NP * (D / 2) : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
@@ -177,6 +184,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   // ---- query fragments (as fwd16_kernel): lane holds q[pos, hh, 16ks + 8g .. +7]
   v8 qf[NQB][NKS];
   {
+    if constexpr (TAB_LDS) {
+      // rows p0 .. p0+NP-1 of the query positions (table rows off + p), the
+      // pairs of row r stored at slot j ^ (r & 15): a wave's read of one
+      // pair for 16 consecutive rows then touches 16 distinct bank groups.
+      // Rows past the table's end (positions >= Sq) read as zero.
+      constexpr int TCH = NP * (D / 2) / 256;  // 16-byte slots per thread
+      const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(tab + (long long)(off + p0) * (D / 2)), (short)0,
+          (uint32_t)(Sq - p0) * (uint32_t)(D / 2) * 16u, kBufferWord3);
+      uint32_t toff[TCH];
+#pragma unroll
+      for (int i = 0; i < TCH; ++i) {
+        const int sl = (w * TCH + i) * 64 + lane, r = sl / (D / 2), pj = sl % (D / 2);
+        toff[i] = (uint32_t)(r * (D / 2) + (pj ^ (r & 15))) * 16u;
+      }
+      dma_rows<TCH>(rt, reinterpret_cast<u16*>(Ts) + w * TCH * 64 * 8, toff, 0u);
+    }
     u32x4 qw[NQB][NKS];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -186,7 +210,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
       for (int ks = 0; ks < NKS; ++ks) qw[qb][ks] = *reinterpret_cast<const u32x4*>(qp + ks * 16);
     }
     double2 cs[NQB][NKS][4];
-    if constexpr (ROPE) {
+    if constexpr (ROPE && !TAB_LDS) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         const double2* tp =
@@ -197,10 +221,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
           for (int e = 0; e < 4; ++e) cs[qb][ks][e] = tp[ks * 8 + e];
       }
     }
+    if constexpr (TAB_LDS) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's table slots (and Q)
+      __syncthreads();                          // every wave's
+    }
     if (nt > 0) {
       load_k(0, Ks0);
       load_v(0, Vs0);
       if (nt > 1) load_k(1, Ks1);
+    }
+    if constexpr (TAB_LDS) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int r = pos[qb] - p0;  // < NP
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            cs[qb][ks][e] = Ts[r * (D / 2) + ((ks * 8 + g * 4 + e) ^ (r & 15))];
+      }
     }
     if constexpr (ROPE) {
 #pragma unroll
@@ -519,10 +558,10 @@ static hipError_t gop(const void* q, const void* k, const void* v, void* o, floa
   const int n_bh = B * (Hq / HPW);
   const long long nblocks = (long long)n_qt * n_bh;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  fwdp_kernel<T, D, HPW, CAUSAL, ROPE, NQB><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
-      static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v),
-      static_cast<u16*>(o), lse, Hq, Hkv, Sq, Skv, kv_lens, kv_rows, scale * kLog2e, tab, n_qt,
-      n_bh);
+  launch_kernel(fwdp_kernel<T, D, HPW, CAUSAL, ROPE, NQB>, dim3((unsigned)nblocks), dim3(256),
+                stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                static_cast<const u16*>(v), static_cast<u16*>(o), lse, Hq, Hkv, Sq, Skv, kv_lens,
+                kv_rows, scale * kLog2e, tab, n_qt, n_bh);
   return hipGetLastError();
 }
 

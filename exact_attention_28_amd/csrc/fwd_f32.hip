@@ -220,11 +220,11 @@ static hipError_t go_f32_lpr(const void* q, const void* k, const void* v, void* 
   const float* kf = static_cast<const float*>(k);
   const float* vf = static_cast<const float*>(v);
   if (mask.p != nullptr)
-    fwd_f32_kernel<D, CAUSAL, ROPE, LPR, true><<<grid, dim3(128), 0, stream>>>(
-        qf, kf, vf, static_cast<float*>(o), lse, Hq, Hkv, Sq, Skv, scale * kLog2e, tab, mask);
+    launch_kernel(fwd_f32_kernel<D, CAUSAL, ROPE, LPR, true>, grid, dim3(128), stream, qf, kf, vf,
+                  static_cast<float*>(o), lse, Hq, Hkv, Sq, Skv, scale * kLog2e, tab, mask);
   else
-    fwd_f32_kernel<D, CAUSAL, ROPE, LPR, false><<<grid, dim3(128), 0, stream>>>(
-        qf, kf, vf, static_cast<float*>(o), lse, Hq, Hkv, Sq, Skv, scale * kLog2e, tab, mask);
+    launch_kernel(fwd_f32_kernel<D, CAUSAL, ROPE, LPR, false>, grid, dim3(128), stream, qf, kf, vf,
+                  static_cast<float*>(o), lse, Hq, Hkv, Sq, Skv, scale * kLog2e, tab, mask);
   return hipGetLastError();
 }
 

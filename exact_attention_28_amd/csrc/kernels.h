@@ -1,10 +1,39 @@
 // kernels.h — host-side launchers of the gfx950 kernels (internal to libattn.so).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
 namespace xattn {
+
+// Event pair that the forward-kernel launches of the calling thread record
+// while the library's kernel-timing session brackets them: the first launch
+// records `start` as the kernel begins, every launch records `stop` as it
+// ends.  The events ride on the dispatch itself (hipExtLaunchKernel), so no
+// marker packet sits between the kernel and the work before it.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+inline LaunchEvents& launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+
+// kernel<<<grid, block, 0, stream>>>(args...), recording the thread's launch
+// events when a timing session has set them.
+template <typename... P, typename... A>
+inline void launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                          A... args) {
+  LaunchEvents& ev = launch_events();
+  if (ev.stop == nullptr) {
+    kernel<<<grid, block, 0, stream>>>(static_cast<P>(args)...);
+    return;
+  }
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0,
+                        static_cast<P>(args)...);
+  ev.start = nullptr;
+}
 
 // Additive fp32 mask for the forward: element (b, h, i, j) at
 // p[b*bs + h*hs + i*rs + j] (strides in elements; 0 broadcasts), added to the

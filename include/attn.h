@@ -301,11 +301,13 @@ const char* attn_last_error(void);
  * up to three kernels (the RoPE table build, the key rotation, the attention
  * kernel); a caller's events around the call time all of them.  Between
  * attn_profile_begin() and attn_profile_end(), every attn_fwd,
- * attn_fwd_masked and attn_prefill_kvcache call records a pair of HIP events
- * on its own stream immediately before and after the launch of its attention
- * kernel (with the key-split merge when the keys are split), so their
- * difference is that kernel's GPU time.  Calls on a stream being captured
- * into a graph record nothing.
+ * attn_fwd_masked and attn_prefill_kvcache call has its attention kernel
+ * (with the key-split merge when the keys are split) record a pair of HIP
+ * events on the call's stream, attached to the kernel dispatches themselves
+ * (hipExtLaunchKernel): start as the kernel begins, stop as the last one
+ * ends, so their difference is that kernel's GPU time, and no marker packet
+ * delays the kernel.  The events carry no system-scope fence.  Calls on a
+ * stream being captured into a graph record nothing.
  *   attn_profile_begin: starts a session (drops one still open).  Returns
  *     ATTN_OK, or ATTN_ERR_HIP if events cannot be created later.
  *   attn_profile_end: waits for the recorded events, writes up to `cap`

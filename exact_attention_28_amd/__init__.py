@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   attn_bwd(q, k, v, o, dout, lse, causal=False, scale=None, rope_base=0.0, ...)
   attn_prefill_kvcache(q, k_new, v_new, kcache, vcache, cache_lens, ...)
   attn_decode_splitkv(q, kcache, vcache, seqlens, num_splits, scale=None, ...)
+  attn_decode_splitkv_noalloc(q, kcache, vcache, seqlens, num_splits, o, ...)
   rope_apply(x, pos_offset=0, rope_base=10000.0)
   attn_decode_workspace_bytes(B, Hq, D, num_splits)
   attn_profile_begin(), attn_profile_end() -> per-launch attention-kernel ms
@@ -28,7 +29,8 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_EMPTY_KV = 0, -1, -2, -3, -4
 EXPORTS = ("attn_fwd", "attn_fwd_masked", "attn_bwd_workspace_bytes", "attn_bwd",
-           "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_prefill_kvcache",
+           "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_noalloc",
+           "attn_prefill_kvcache",
            "rope_apply", "attn_last_error", "attn_profile_begin", "attn_profile_end")
 
 _lib = None
@@ -64,6 +66,8 @@ def load():
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp]
     lib.attn_decode_splitkv.restype = i
+    lib.attn_decode_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp]
+    lib.attn_decode_splitkv_noalloc.restype = i
     lib.attn_prefill_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
                                          f, vp]
     lib.attn_prefill_kvcache.restype = i
@@ -293,6 +297,32 @@ def attn_decode_splitkv(q, kcache, vcache, seqlens, num_splits, scale=None, o=No
     _check(load().attn_decode_splitkv(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(o),
                                       B, Hq, Hkv, D, int(num_splits), float(scale), Smax,
                                       _ptr(lse), _ptr(workspace), _stream(stream)))
+    return o, lse
+
+
+def attn_decode_splitkv_noalloc(q, kcache, vcache, seqlens, num_splits, o, lse=None, scale=None,
+                                stream=None):
+    """attn_decode_splitkv with the partials in the library's built-in
+    scratch (no device allocation by the library; o, and lse if wanted, are
+    the caller's).  Returns (o, lse)."""
+    _need_gpu(q, kcache, vcache, seqlens, o, lse)
+    B, Hq, D = q.shape
+    Bk, Smax, Hkv, Dk = kcache.shape
+    if tuple(vcache.shape) != tuple(kcache.shape) or Bk != B or Dk != D:
+        raise ValueError("shape mismatch between q and the caches")
+    if seqlens.dtype != torch.int32 or seqlens.numel() != B:
+        raise ValueError("seqlens must be int32 [B]")
+    if q.dtype != torch.bfloat16 or kcache.dtype != torch.bfloat16 or vcache.dtype != torch.bfloat16:
+        raise TypeError("decode takes bf16 q and caches")
+    if o is None:
+        raise ValueError("o is required (this entry point allocates nothing)")
+    _check_out(o, "o", q.shape, q.dtype)
+    _check_out(lse, "lse", (B, Hq), torch.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(load().attn_decode_splitkv_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens),
+                                              _ptr(o), B, Hq, Hkv, D, int(num_splits),
+                                              float(scale), Smax, _ptr(lse), _stream(stream)))
     return o, lse
 
 

@@ -408,7 +408,61 @@ int fwd(const char* fn, const void* q, const void* k, const void* v, void* o, fl
   return hip_status(e, "attn_fwd: kernel launch");
 }
 
+// Argument checks shared by the split-KV decode entry points (`fn` names the
+// entry point in messages).
+int check_decode_args(const char* fn, const void* q, const void* kcache, const void* vcache,
+                      const int* seqlens, const void* o, int B, int Hq, int Hkv, int D,
+                      int num_splits, float scale, int max_seqlen) {
+  if (!q || !kcache || !vcache || !seqlens || !o)
+    return fail(ATTN_ERR_INVALID, "%s: null q, kcache, vcache, seqlens or o", fn);
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1)
+    return fail(ATTN_ERR_INVALID, "%s: sizes must be >= 1", fn);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_INVALID, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (num_splits < 1 || num_splits > 64)
+    return fail(ATTN_ERR_INVALID, "%s: num_splits=%d outside [1, 64]", fn, num_splits);
+  if (max_seqlen < 1) return fail(ATTN_ERR_INVALID, "%s: max_seqlen < 1", fn);
+  if (!finite_pos(scale)) return fail(ATTN_ERR_INVALID, "%s: scale must be finite and > 0", fn);
+  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "%s: D=%d (built: 64, 128)", fn, D);
+  if (B > 65535 || Hq > 65535 || (long long)B * Hq > 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  return ATTN_OK;
+}
+
 }  // namespace
+
+// Scratch of attn_decode_splitkv_noalloc: the decode partials live in this
+// array, which the code object brings into every GPU's memory when the
+// library is loaded there (each GPU holds its own copy, at its own address,
+// until the process ends).  In host code `scratch` names a host-side stand-in,
+// not device memory: kernels and copies get the per-device address that
+// hipGetSymbolAddress returns, fetched once per device on the entry point's
+// first call there.
+static constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+static std::mutex g_scratch_mu;
+static std::map<int, void*> g_scratch_ptr;  // device -> device address of `scratch`
+
+// Device address of `scratch` on the current device (looked up once per device).
+static int scratch_on_device(const char* fn, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *ptr = it->second;
+    return ATTN_OK;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || p == nullptr)
+    return fail(ATTN_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                hipGetErrorString(e));
+  g_scratch_ptr[dev] = p;
+  *ptr = p;
+  return ATTN_OK;
+}
 
 extern "C" {
 
@@ -532,23 +586,9 @@ int attn_decode_splitkv(const void* q, const void* kcache, const void* vcache,
                         const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
                         int num_splits, float scale, int max_seqlen, float* lse,
                         void* workspace, hipStream_t stream) {
-  if (!q || !kcache || !vcache || !seqlens || !o)
-    return fail(ATTN_ERR_INVALID, "attn_decode_splitkv: null q, kcache, vcache, seqlens or o");
-  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1)
-    return fail(ATTN_ERR_INVALID, "attn_decode_splitkv: sizes must be >= 1");
-  if (Hq % Hkv != 0)
-    return fail(ATTN_ERR_INVALID, "attn_decode_splitkv: Hq=%d is not a multiple of Hkv=%d", Hq,
-                Hkv);
-  if (num_splits < 1 || num_splits > 64)
-    return fail(ATTN_ERR_INVALID, "attn_decode_splitkv: num_splits=%d outside [1, 64]",
-                num_splits);
-  if (max_seqlen < 1) return fail(ATTN_ERR_INVALID, "attn_decode_splitkv: max_seqlen < 1");
-  if (!finite_pos(scale))
-    return fail(ATTN_ERR_INVALID, "attn_decode_splitkv: scale must be finite and > 0");
-  if (D != 64 && D != 128)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_splitkv: D=%d (built: 64, 128)", D);
-  if (B > 65535 || Hq > 65535 || (long long)B * Hq > 0x7fffffffLL)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_splitkv: grid too large");
+  if (int st = check_decode_args("attn_decode_splitkv", q, kcache, vcache, seqlens, o, B, Hq, Hkv,
+                                 D, num_splits, scale, max_seqlen))
+    return st;
   if (int st = debug_check_lens("attn_decode_splitkv", "seqlens", seqlens, B, 0, max_seqlen,
                                 stream))
     return st;
@@ -568,6 +608,29 @@ int attn_decode_splitkv(const void* q, const void* kcache, const void* vcache,
   hipError_t e = xattn::launch_decode(q, kcache, vcache, seqlens, o, lse, B, Hq, Hkv, D,
                                       num_splits, scale, max_seqlen, ws, stream);
   return hip_status(e, "attn_decode_splitkv: kernel launch");
+}
+
+int attn_decode_splitkv_noalloc(const void* q, const void* kcache, const void* vcache,
+                                const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
+                                int num_splits, float scale, int max_seqlen, float* lse,
+                                hipStream_t stream) {
+  const char* fn = "attn_decode_splitkv_noalloc";
+  if (int st = check_decode_args(fn, q, kcache, vcache, seqlens, o, B, Hq, Hkv, D, num_splits,
+                                 scale, max_seqlen))
+    return st;
+  const size_t need = xattn::decode_workspace_bytes(B, Hq, D, num_splits);
+  if (need > kNoAllocScratchBytes)
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "%s: the partials need %zu bytes (B*Hq*num_splits*(D+1)*4, rounded to 256); the "
+                "built-in scratch holds %zu",
+                fn, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (int st = scratch_on_device(fn, &ws)) return st;
+  // every split writes its partial (an empty one too), so the scratch needs
+  // no clearing between calls
+  hipError_t e = xattn::launch_decode(q, kcache, vcache, seqlens, o, lse, B, Hq, Hkv, D,
+                                      num_splits, scale, max_seqlen, ws, stream);
+  return hip_status(e, "attn_decode_splitkv_noalloc: kernel launch");
 }
 
 int attn_prefill_kvcache(const void* q, const void* k_new, const void* v_new, void* kcache,

@@ -241,6 +241,32 @@ int attn_decode_splitkv(const void* q, const void* kcache, const void* vcache,
                         void* workspace, hipStream_t stream);
 
 /*
+ * attn_decode_splitkv_noalloc — attn_decode_splitkv for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): it allocates nothing (no hipMalloc,
+ * hipFree or allocating library call) and keeps the per-split partials in a
+ * scratch array built into the library, 16 MiB per GPU, which each GPU the
+ * library runs on holds until the process ends.
+ *
+ * Arguments, result and errors are those of attn_decode_splitkv without the
+ * workspace (and without the ATTN_DEBUG length check, which copies to the
+ * host); the same kernels run, so o and lse are bit-identical to
+ * attn_decode_splitkv's.  Shapes whose partials need more than the scratch,
+ * attn_decode_workspace_bytes(B, Hq, D, num_splits) > 16 MiB (for example
+ * B*Hq*num_splits > 32513 at D = 128), return ATTN_ERR_UNSUPPORTED and launch
+ * nothing.  Every call on one GPU uses that GPU's one scratch array and leaves
+ * its partials there (every split of a call writes its own, so nothing needs
+ * clearing): calls that can overlap on one GPU (different streams, or
+ * different host threads) race and must be serialised by the caller.  The
+ * first call on a device looks the array's address up there
+ * (hipGetSymbolAddress); ATTN_ERR_HIP if that fails.
+ */
+int attn_decode_splitkv_noalloc(const void* q, const void* kcache, const void* vcache,
+                                const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
+                                int num_splits, float scale, int max_seqlen, float* lse,
+                                hipStream_t stream);
+
+/*
  * attn_prefill_kvcache — one chunk of a streaming (chunked) prefill against a
  * token-major KV cache: append, then attend.
  *

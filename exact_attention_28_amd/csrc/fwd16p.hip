@@ -222,10 +222,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
       }
     }
     if constexpr (TAB_LDS) {
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's table slots (and Q)
-      __syncthreads();                          // every wave's
-    }
-    if (nt > 0) {
+      // the first K and V tiles go out behind the table and Q (a second K
+      // tile past the keys reads zeros into a buffer no step then reads);
+      // loads complete in issue order, so waiting until only those 3 LD are
+      // outstanding covers this wave's table slots, and the barrier every
+      // wave's
+      static_assert(3 * LD <= 15, "vmcnt immediate");
+      load_k(0, Ks0);
+      load_v(0, Vs0);
+      load_k(1, Ks1);
+      // (a bare barrier: __syncthreads would add a release fence that waits
+      // for every outstanding load, the K and V tiles included)
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | (3 * LD));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    } else if (nt > 0) {
       load_k(0, Ks0);
       load_v(0, Vs0);
       if (nt > 1) load_k(1, Ks1);

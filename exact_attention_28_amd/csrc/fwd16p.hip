@@ -398,14 +398,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   // then the PV products) and its share of the softmax's vector
   // instructions; a scheduling barrier after each slot keeps that order
   // (the scheduler would otherwise issue the products back to back).
-  auto step = [&](f32x16(&s_sm)[NQB], int k0, u32x4(&p_out)[NQB][2], auto do_qk,
+  auto step = [&](auto do_mask, f32x16(&s_sm)[NQB], int k0, u32x4(&p_out)[NQB][2], auto do_qk,
                   f32x16(&s_qk)[NQB], const u16* kb, int khb, auto do_pv,
                   const u32x4(&p_in)[NQB][2], const u16* vb, int vhb)
                   __attribute__((always_inline)) {
     constexpr bool DQ = decltype(do_qk)::value, DP = decltype(do_pv)::value;
     constexpr int NQK = DQ ? NKS * NQB : 0, NPV = DP ? 2 * NDB * NQB : 0, NM = NQK + NPV;
     constexpr int NE = NQB * 16;  // scores per lane in the half
-    mask_half(s_sm, k0);
+    if constexpr (decltype(do_mask)::value) mask_half(s_sm, k0);
     float ls[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) ls[qb] = 0.f;
@@ -509,30 +509,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const int kbase = 0;  // first key of the workgroup's range
     // prologue: S of half 0, then its softmax with the products of half 1
     qk(Ks0, 0, sA);
-    step(sA, kbase, pA, Y, sB, Ks0, 1, N, pB, Vs0, 0);
+    step(Y, sA, kbase, pA, Y, sB, Ks0, 1, N, pB, Vs0, 0);
     __syncthreads();  // every wave has read K tile 0 (its buffer takes tile 2)
     // tile-step pairs: halves 2u+1 and 2u+2 read K tile u+1 and V tile u
-    auto pair = [&](int u, u16* kcur, u16* knext, u16* vcur, u16* vnext)
+    auto pair = [&](auto do_mask, int u, u16* kcur, u16* knext, u16* vcur, u16* vnext)
                     __attribute__((always_inline)) {
       // (issuing these one instruction per slot instead, to keep the
       // address unit busy evenly, measured no faster)
       if (u + 2 < nt) load_k(u + 2, knext);  // into the buffer K tile u used
       load_v(u + 1, vnext);                  // into the buffer V tile u-1 used
       const int k1 = kbase + u * BN + 32;
-      step(sB, k1, pB, Y, sA, kcur, 0, Y, pA, vcur, 0);
-      step(sA, k1 + 32, pA, Y, sB, kcur, 1, Y, pB, vcur, 1);
+      step(do_mask, sB, k1, pB, Y, sA, kcur, 0, Y, pA, vcur, 0);
+      step(do_mask, sA, k1 + 32, pA, Y, sB, kcur, 1, Y, pB, vcur, 1);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
     };
+    // Halves 0 .. h_open-1 (first key 32 h) need no mask: every key of
+    // them is below Skv and (causal) at or before the workgroup's first
+    // query.  Masking is monotone in the key, so the pairs run first
+    // without the mask test while both of a double pair's halves are below
+    // h_open, then with it.
+    const int kmax = CAUSAL ? min(first_q, Skv - 1) : Skv - 1;  // last key every column sees
+    const int h_open = kmax >= 31 ? (kmax + 1) / 32 : 0;
     // pair u reads K tile u+1 from buffer (u+1) & 1 and V tile u from u & 1
-    for (int u = 0; u + 1 < nt; u += 2) {
-      pair(u, Ks1, Ks0, Vs0, Vs1);
-      if (u + 2 < nt) pair(u + 1, Ks0, Ks1, Vs1, Vs0);
+    int u = 0;
+    for (; u + 2 < nt && 2 * u + 5 <= h_open; u += 2) {
+      pair(N, u, Ks1, Ks0, Vs0, Vs1);
+      pair(N, u + 1, Ks0, Ks1, Vs1, Vs0);
+    }
+    for (; u + 1 < nt; u += 2) {
+      pair(Y, u, Ks1, Ks0, Vs0, Vs1);
+      if (u + 2 < nt) pair(Y, u + 1, Ks0, Ks1, Vs1, Vs0);
     }
     // epilogue: softmax of the last half with the PV of the one before, then
     // the PV of the last half (V tile nt-1 in buffer (nt-1) & 1)
     const u16* vlast = ((nt - 1) & 1) ? Vs1 : Vs0;
-    step(sB, kbase + (nt - 1) * BN + 32, pB, N, sA, Ks0, 0, Y, pA, vlast, 0);
+    step(Y, sB, kbase + (nt - 1) * BN + 32, pB, N, sA, Ks0, 0, Y, pA, vlast, 0);
     pv(vlast, 1, pB);
   }
 

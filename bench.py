@@ -17,7 +17,7 @@ event on MI355X, ~5 us with the default system-scope fence), so no event
 sits inside either run.  `value` is the prefill throughput in TFLOP/s
 (algorithmic flops 4*B*Hq*S*S*D/2 over the mean attn_fwd call of the timed
 prefill run: key rotation + attention kernel); the decode KV-read bandwidth
-(median of 50 calls, each after a 512 MiB flush write) and both fractions of
+(median of 50 calls, each after a 512 MiB read flush) and both fractions of
 peak sit beside it.  The `roofline` object is for the dominant kernel, the
 fused RoPE attention kernel of the headline call, timed by the HIP event
 pair that the library attaches to that kernel's dispatch
@@ -239,12 +239,13 @@ COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
 FLUSH_BYTES = 512 << 20  # written between decode repetitions (twice the 256 MiB MALL)
 
 
-def profile_kernel(reps, workload):
-    """For trace and counter runs: `reps` production attn_fwd calls on the
-    named prefill workload (default the LFM2 prefill: RoPE table once, then
-    per call the key rotation and the fused attention kernel), after one
-    untimed call, then `reps` launches of a plain elementwise copy of
-    COPY_BYTES (dst = src + 0) for calibration."""
+def profile_kernel(reps, workload, settle_s=0.5):
+    """For trace and counter runs: production attn_fwd calls on the named
+    prefill workload (default the LFM2 prefill: RoPE table once, then per
+    call the key rotation and the fused attention kernel), back to back for
+    `settle_s` seconds so the clocks settle and then `reps` more (every call
+    is the same production call), then `reps` launches of a plain
+    elementwise copy of COPY_BYTES (dst = src + 0) for calibration."""
     pc = {c.name: c for c in W.PREFILL}[workload]
     q_np, k_np, v_np = W.prefill_inputs(pc)
     q, k, v = W.to_device(q_np), W.to_device(k_np), W.to_device(v_np)
@@ -252,12 +253,14 @@ def profile_kernel(reps, workload):
     lse = torch.empty((pc.B, pc.Hq, pc.Sq), dtype=torch.float32, device="cuda")
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    xa.attn_fwd(q, k, v, causal=pc.causal, scale=pc.scale, rope_base=pc.rope_base, o=o, lse=lse)
-    torch.cuda.synchronize()
-    for _ in range(reps):
+    def call():
         xa.attn_fwd(q, k, v, causal=pc.causal, scale=pc.scale, rope_base=pc.rope_base, o=o,
                     lse=lse)
+    n_settle = settle(call, settle_s)
+    for _ in range(reps):
+        call()
     torch.cuda.synchronize()
+    log(f"profile-kernel: {n_settle} settle calls, then {reps} calls")
     for _ in range(reps):
         torch.add(src, 0.0, out=dst)
     torch.cuda.synchronize()
@@ -265,9 +268,10 @@ def profile_kernel(reps, workload):
 
 
 def profile_decode(reps, ns=16):
-    """For trace and counter runs: `reps` split-KV decode calls (split +
-    merge, `ns` splits) on the decode workload, then `reps` launches of the
-    calibration copy."""
+    """For trace and counter runs: split-KV decode calls (split + merge, `ns`
+    splits) on the decode workload, back to back for 0.3 s and then `reps`
+    more (all at `ns` splits), then `reps` launches of the calibration
+    copy."""
     dc = W.C5
     dq_np, kc_np, vc_np, sl_np = W.decode_inputs(dc)
     dq, kc, vc = W.to_device(dq_np), W.to_device(kc_np), W.to_device(vc_np)
@@ -277,10 +281,13 @@ def profile_decode(reps, ns=16):
                      device="cuda")
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    torch.cuda.synchronize()
-    for _ in range(reps):
+    def call():
         xa.attn_decode_splitkv(dq, kc, vc, sl, ns, scale=dc.scale, o=do, workspace=ws)
+    n_settle = settle(call, 0.3)
+    for _ in range(reps):
+        call()
     torch.cuda.synchronize()
+    log(f"profile-decode: {n_settle} settle calls, then {reps} calls at {ns} splits")
     for _ in range(reps):
         torch.add(src, 0.0, out=dst)
     torch.cuda.synchronize()
@@ -335,6 +342,46 @@ def counters_summary(csv_path, match, out_path, title, cmds):
             fac = COPY_BYTES / 1024 / np.mean(copy[cn])
             lines.append(f"{cn}_bytes_per_dispatch_scaled: {np.mean(vals[cn]) * fac * 1024:.0f}"
                          f"  (scale {fac:.4f})")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def stats_summary(csv_path, out_path, title, cmds):
+    """Writes a per-kernel table (calls, average / min / max duration in us,
+    share of the total) from a rocprofv3 --stats kernel_stats.csv."""
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+
+    def col(r, *names):
+        for n in names:
+            if n in r:
+                return r[n]
+        raise KeyError(names)
+    table = []
+    for r in rows:
+        table.append((col(r, "Name", "KernelName", "Kernel_Name"), int(float(col(r, "Calls"))),
+                      float(col(r, "AverageNs")) / 1e3, float(col(r, "MinNs")) / 1e3,
+                      float(col(r, "MaxNs")) / 1e3, float(col(r, "Percentage"))))
+    table.sort(key=lambda t: -t[1] * t[2])
+    try:  # readable names (the trace keeps some mangled); argument lists dropped
+        import subprocess
+        # this c++filt does not know the __bf16 / _Float16 manglings: spell
+        # them as vendor types it prints by name
+        raw = [t[0].replace("DF16b", "u6__bf16").replace("DF16_", "u8_Float16") for t in table]
+        dem = subprocess.run(["c++filt"], input="\n".join(raw), text=True,
+                             capture_output=True, check=True).stdout.splitlines()
+        dem = [d[5:] if d.startswith("void ") else d for d in dem]
+        table = [(d.split("(")[0] if "<" in d else d,) + t[1:] for d, t in zip(dem, table)]
+    except (OSError, subprocess.CalledProcessError):
+        pass
+    lines = [f"# {title}", "# Commands (from the repository root, TMPDIR=/tmp):",
+             *[f"#   {c}" for c in cmds], "# Durations are per dispatch, in microseconds.", "",
+             f"{'kernel':90s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} "
+             f"{'share%':>7s}"]
+    for name, calls, avg, mn, mx, share in table:
+        short = name if len(name) <= 90 else name[:87] + "..."
+        lines.append(f"{short:90s} {calls:6d} {avg:9.2f} {mn:9.2f} {mx:9.2f} {share:7.2f}")
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -401,6 +448,8 @@ def main():
                     help="prefill workload of --profile-kernel")
     ap.add_argument("--profile-kernel", type=int, default=0, metavar="REPS",
                     help="only launch the prefill kernel REPS times, then a calibration copy")
+    ap.add_argument("--profile-settle", type=float, default=0.5, metavar="SECONDS",
+                    help="untimed production calls before --profile-kernel's REPS")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 counter CSVs")
     ap.add_argument("--traffic-cmd", action="append", default=[],
@@ -413,12 +462,17 @@ def main():
                     help="only run the LFM2 prefill backward REPS times")
     ap.add_argument("--counters-summary", nargs=4, metavar=("CSV", "MATCH", "OUT", "TITLE"),
                     help="write per-dispatch counter means of kernels matching MATCH")
+    ap.add_argument("--stats-summary", nargs=3, metavar=("CSV", "OUT", "TITLE"),
+                    help="write the per-kernel table of a rocprofv3 --stats kernel_stats.csv")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary, TRAFFIC_FILE, args.traffic_cmd)
         return
     if args.counters_summary:
         counters_summary(*args.counters_summary, args.traffic_cmd)
+        return
+    if args.stats_summary:
+        stats_summary(*args.stats_summary, args.traffic_cmd)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
@@ -427,7 +481,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     if args.profile_kernel:
-        profile_kernel(args.profile_kernel, args.profile_workload)
+        profile_kernel(args.profile_kernel, args.profile_workload, args.profile_settle)
         return
     if args.profile_decode:
         profile_decode(args.profile_decode, args.profile_splits)
@@ -467,11 +521,15 @@ def main():
 
     # ---- warmup, and the split count for the decode half (outside the timed
     # region): each count timed as the decode record below is, median of
-    # calls with a 512 MiB flush write before each
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    # calls with a 512 MiB read flush before each: a reduction over a
+    # 512 MiB buffer (twice the MALL) evicts the caches without leaving
+    # dirty lines behind (a write flush would leave the MALL full of them,
+    # and their write-back would then compete with the decode's reads)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    flush_sink = torch.empty((), dtype=torch.float32, device="cuda")
 
     def flush_caches():
-        flush.fill_(1.0)
+        torch.sum(flush, out=flush_sink)
 
     log("warmup")
     for _ in range(max(args.warmup, 1)):
@@ -504,7 +562,7 @@ def main():
     pre_tflops = pc.flops / (pre_ms * 1e-3) / 1e12
 
     # ---- decode as the measurement protocol times it: 50 calls at the chosen
-    # split count, each after a 512 MiB flush write (outside its events), median
+    # split count, each after a 512 MiB read flush (outside its events), median
     settle(lambda: decode(best_ns), args.settle / 5)
     dec_ms = timed(lambda: decode(best_ns), 50, stream, flush_caches)
     dec_gbps = kv_bytes / (dec_ms * 1e-3) / 1e9
@@ -637,7 +695,7 @@ def main():
                     "tflops": round(pre_tflops, 2),
                     "frac_of_mfma_peak": round(pre_tflops / PEAK_BF16_TFLOPS, 4)},
         "decode": {"what": f"attn_decode_splitkv (split + merge) at {best_ns} splits, 50 calls "
-                           f"each after a {FLUSH_BYTES >> 20} MiB flush write outside the "
+                           f"each after a {FLUSH_BYTES >> 20} MiB read flush outside the "
                            "events, median",
                    "ms": round(dec_ms, 4), "GBps": round(dec_gbps, 1),
                    "frac_of_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),

@@ -62,8 +62,8 @@ namespace xattn {
 // A lane's sum of probabilities over a half above which the reference moves.
 constexpr float kRefWindow = 0x1p8f;
 
-template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fwdp_kernel(
+template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB, int KS>
+__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2))) void fwdp_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Skv_all,
     const int* __restrict__ kv_lens, int kv_rows, float scale_log2,
@@ -77,10 +77,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   typedef Fmt16<T> F;
   typedef typename F::v8 v8;
 
-  __shared__ __attribute__((aligned(16))) u16 Ks0[BN * D];
-  __shared__ __attribute__((aligned(16))) u16 Vs0[BN * D];
-  __shared__ __attribute__((aligned(16))) u16 Ks1[BN * D];
-  __shared__ __attribute__((aligned(16))) u16 Vs1[BN * D];
+  // K and V double buffers of each key group (KS groups of 4 waves; see below)
+  __shared__ __attribute__((aligned(16))) u16 Ks0g[KS][BN * D];
+  __shared__ __attribute__((aligned(16))) u16 Vs0g[KS][BN * D];
+  __shared__ __attribute__((aligned(16))) u16 Ks1g[KS][BN * D];
+  __shared__ __attribute__((aligned(16))) u16 Vs1g[KS][BN * D];
   // RoPE (cos, sin) rows of the workgroup's NP positions, loaded once and
   // read by every wave (the HPW heads of a position share its row) when the
   // workgroup's LDS stays within 80 KiB (two workgroups per CU); otherwise
@@ -89,8 +90,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
                            (NP * D / 2) % 256 == 0;
   __shared__ __attribute__((aligned(16))) double2 Ts[TAB_LDS ? NP * (D / 2) : 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // KS = 2 (launches with fewer workgroups than CUs): two groups of 4 waves
+  // take the two halves of the workgroup's key tiles for the same query
+  // columns, with their own K/V buffers, and merge (m, l, O) through LDS at
+  // the end.  Both groups run the same number of pairs (the second group's
+  // last tiles may lie past the keys: range-checked loads read zeros there
+  // and the mask drops them), so they meet at every barrier.
+  const int tid = threadIdx.x, lane = tid & 63, w = (tid >> 6) & 3;
+  const int grp = KS > 1 ? (tid >> 8) : 0;
   const int c = lane & 31, g = lane >> 5;
+  u16* const Ks0 = Ks0g[grp];
+  u16* const Vs0 = Vs0g[grp];
+  u16* const Ks1 = Ks1g[grp];
+  u16* const Vs1 = Vs1g[grp];
 
   // block -> (query tile, batch-head group); the group varies fastest (one
   // XCD per group), query tiles heaviest first under causal
@@ -118,7 +130,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 
   int kv_end = Skv;
   if (CAUSAL) kv_end = min(Skv, min(p0 + NP, Sq) - 1 + off + 1);
-  const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;  // 64-key tiles
+  const int nt_all = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;  // 64-key tiles
+  const int nt = (nt_all + KS - 1) / KS;  // tiles of this wave's key group
+  const int t0 = grp * nt;                // its first tile
   const int first_q = p0 + off;
 
   const long long head_base = (long long)b * kv_rows * Hkv * D + (long long)kvh * D;
@@ -137,11 +151,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     voff[i] = (uint32_t)row * row_bytes + (uint32_t)(phys ^ vswz<D>(row)) * 16u;
   }
   // direct loads of key tile u into kb / value tile u into vb (this wave's share)
+  // (u counts the group's tiles)
   auto load_k = [&](int u, u16* kb) {
-    dma_rows<LD>(rk, kb + w * LD * 64 * 8, koff, (uint32_t)(u * BN) * row_bytes);
+    dma_rows<LD>(rk, kb + w * LD * 64 * 8, koff, (uint32_t)((t0 + u) * BN) * row_bytes);
   };
   auto load_v = [&](int u, u16* vb) {
-    dma_rows<LD>(rv, vb + w * LD * 64 * 8, voff, (uint32_t)(u * BN) * row_bytes);
+    dma_rows<LD>(rv, vb + w * LD * 64 * 8, voff, (uint32_t)((t0 + u) * BN) * row_bytes);
   };
   // K fragment of half hb, k-step ks: row 32 hb + c, logical chunk 2 ks + g.
   // The swizzle of row 32 hb + c does not depend on hb, so a half's
@@ -506,7 +521,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const std::false_type N;
     f32x16 sA[NQB], sB[NQB];
     u32x4 pA[NQB][2], pB[NQB][2];
-    const int kbase = 0;  // first key of the workgroup's range
+    const int kbase = t0 * BN;  // first key of the group's range
     // prologue: S of half 0, then its softmax with the products of half 1
     qk(Ks0, 0, sA);
     step(Y, sA, kbase, pA, Y, sB, Ks0, 1, N, pB, Vs0, 0);
@@ -533,7 +548,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const int h_open = kmax >= 31 ? (kmax + 1) / 32 : 0;
     // pair u reads K tile u+1 from buffer (u+1) & 1 and V tile u from u & 1
     int u = 0;
-    for (; u + 2 < nt && 2 * u + 5 <= h_open; u += 2) {
+    for (; u + 2 < nt && 2 * (t0 + u) + 5 <= h_open; u += 2) {
       pair(N, u, Ks1, Ks0, Vs0, Vs1);
       pair(N, u + 1, Ks0, Ks1, Vs1, Vs0);
     }
@@ -547,6 +562,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     step(Y, sB, kbase + (nt - 1) * BN + 32, pB, N, sA, Ks0, 0, Y, pA, vlast, 0);
     pv(vlast, 1, pB);
   }
+
+  if constexpr (KS > 1) {
+    // the second key group's (m, l, O) into the first's: lane (w, lane) of
+    // both groups holds the same query column.  The exchange reuses the K/V
+    // buffers once every wave's last reads of them are done: O block db of
+    // the group's 4 waves (16 KiB) at float (16 (db mod NDB/2) + r) * 256 +
+    // 64 w + lane of Ks0g (db < NDB/2) or Vs0g, m and l in Ks1g.
+    static_assert(KS == 2 && NQB == 1 && !ROPE && NDB % 2 == 0, "key groups");
+    static_assert(16 * 256 * 4 * (NDB / 2) <= (int)sizeof(Ks0g), "exchange space");
+    float* const xo0 = reinterpret_cast<float*>(&Ks0g[0][0]);
+    float* const xo1 = reinterpret_cast<float*>(&Vs0g[0][0]);
+    float* const xml = reinterpret_cast<float*>(&Ks1g[0][0]);
+    const int xl = w * 64 + lane;
+    __syncthreads();
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          (db < NDB / 2 ? xo0 : xo1)[(16 * (db % (NDB / 2)) + r) * 256 + xl] = oacc[0][db][r];
+      xml[xl] = m_run[0];
+      xml[256 + xl] = l_run[0];
+    }
+    __syncthreads();
+    if (grp == 0) {
+      const float m1 = xml[xl], l1 = xml[256 + xl];
+      const float mn = fmaxf(m_run[0], m1);
+      const float a0 = (mn == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[0] - mn);
+      const float a1 = (mn == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - mn);
+      l_run[0] = l_run[0] * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          oacc[0][db][r] = oacc[0][db][r] * a0 +
+                           (db < NDB / 2 ? xo0 : xo1)[(16 * (db % (NDB / 2)) + r) * 256 + xl] * a1;
+      m_run[0] = mn;
+    }
+  }
+  if (KS > 1 && grp != 0) return;
 
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
@@ -573,7 +628,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   }
 }
 
-template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB>
+template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB, int KS>
 static hipError_t gop(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int Hq, int Hkv, int Sq, int Skv, const int* kv_lens, int kv_rows,
                       float scale, const double2* tab, hipStream_t stream) {
@@ -582,7 +637,7 @@ static hipError_t gop(const void* q, const void* k, const void* v, void* o, floa
   const int n_bh = B * (Hq / HPW);
   const long long nblocks = (long long)n_qt * n_bh;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  launch_kernel(fwdp_kernel<T, D, HPW, CAUSAL, ROPE, NQB>, dim3((unsigned)nblocks), dim3(256),
+  launch_kernel(fwdp_kernel<T, D, HPW, CAUSAL, ROPE, NQB, KS>, dim3((unsigned)nblocks), dim3(256 * KS),
                 stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
                 static_cast<const u16*>(v), static_cast<u16*>(o), lse, Hq, Hkv, Sq, Skv, kv_lens,
                 kv_rows, scale * kLog2e, tab, n_qt, n_bh);
@@ -599,10 +654,20 @@ static hipError_t gop_nqb(const void* q, const void* k, const void* v, void* o, 
   if constexpr (D == 64) {
     const long long wg2 = (long long)((Sq + 256 / HPW - 1) / (256 / HPW)) * B * (Hq / HPW);
     if (wg2 >= 2 * 256)
-      return gop<T, D, HPW, CAUSAL, ROPE, 2>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
+      return gop<T, D, HPW, CAUSAL, ROPE, 2, 1>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
                                              kv_rows, scale, tab, stream);
   }
-  return gop<T, D, HPW, CAUSAL, ROPE, 1>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
+  // fewer one-block workgroups than CUs and 16 or more key tiles: two key
+  // groups per workgroup (without RoPE).  With fewer tiles the merge and the
+  // second group's prologue cost more than the halved loop saves (1024 query
+  // rows, 8 heads: 512 keys 12.5 -> 13.1 us, 1024 keys 17.3 -> 14.5 us)
+  if constexpr (!ROPE) {
+    const long long wg1 = (long long)((Sq + 128 / HPW - 1) / (128 / HPW)) * B * (Hq / HPW);
+    if (wg1 < 256 && Skv >= 16 * 64)
+      return gop<T, D, HPW, CAUSAL, ROPE, 1, 2>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,
+                                                kv_rows, scale, tab, stream);
+  }
+  return gop<T, D, HPW, CAUSAL, ROPE, 1, 1>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens, kv_rows,
                                          scale, tab, stream);
 }
 

@@ -64,6 +64,7 @@ F16_CASES = [  # B, Hq, Hkv, Sq, Skv, D, causal, rope
     (1, 16, 2, 129, 129, 128, True, 500.0),   # 8 heads per kv head
     (2, 6, 3, 33, 90, 40, False, 10000.0),    # padded head dim
     (4, 4, 4, 600, 600, 64, False, 0.0),      # two query blocks per wave
+    (1, 4, 2, 150, 1090, 64, True, 0.0),      # two key groups per workgroup
 ]
 
 

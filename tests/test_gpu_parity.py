@@ -147,6 +147,13 @@ BF16_CASES = [  # B, Hq, Hkv, Sq, Skv, D, causal, rope, amplitude
     (1, 4, 2, 256, 320, 64, True, 0.0, 4.0),    # scores up to ~±100: the running max moves often
     (64, 1, 1, 33, 33, 64, True, 0.0, 1.0),     # many small (batch, head) units
     (1, 12, 2, 100, 100, 128, True, 10000.0, 1.0),  # 6 query heads per kv head (pairs of heads)
+    # under-filled launches with >= 16 key tiles: two key groups per workgroup
+    # merged through LDS (odd tile counts leave the second group a tile past
+    # the keys; causal rows see only part of the second group's keys)
+    (1, 4, 2, 200, 1100, 64, False, 0.0, 1.0),
+    (1, 4, 4, 150, 1050, 64, True, 0.0, 1.0),
+    (2, 4, 4, 100, 1300, 128, False, 0.0, 1.0),
+    (1, 4, 1, 64, 1024, 64, True, 0.0, 4.0),
 ]
 
 

@@ -529,7 +529,7 @@ def main():
     flush_sink = torch.empty((), dtype=torch.float32, device="cuda")
 
     def flush_caches():
-        torch.sum(flush, out=flush_sink)
+        torch.sum(flush, dim=0, out=flush_sink)
 
     log("warmup")
     for _ in range(max(args.warmup, 1)):

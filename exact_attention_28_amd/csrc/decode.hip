@@ -217,7 +217,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 
 // One wave per (batch, query head): merge the splits by log-sum-exp.  Lane i
 // holds split i's lse and weight exp(lse_i - L); each lane then accumulates
-// its D/64 output elements over the splits.
+// its D/64 output elements over the splits.  The partial outputs of the
+// first kPre splits are loaded together with the lse values, before the
+// weights are known, so the merge waits on one round trip to memory
+// instead of three.
+constexpr int kPre = 16;
+
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws_o,
                                                             const float* __restrict__ ws_lse,
@@ -226,6 +231,12 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   constexpr int PER = D / 64;
   const long long bh = blockIdx.x;
   const int lane = threadIdx.x;
+  const float* op = ws_o + bh * ns * D + lane * PER;
+  float pre[kPre][PER];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) pre[i][e] = (i < ns) ? op[(long long)i * D + e] : 0.f;
   const float li = (lane < ns) ? ws_lse[bh * ns + lane] : -INFINITY;
   const bool fin = li > -INFINITY && li < INFINITY;  // empty splits carry -inf
   float M = fin ? li : -INFINITY;
@@ -241,9 +252,15 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   float o[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  const float* op = ws_o + bh * ns * D + lane * PER;
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    // splits past ns have weight 0 (lanes >= ns carry -inf) and loaded 0
+    const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = fmaf(wi, pre[i][e], o[e]);
+  }
 #pragma unroll 8
-  for (int i = 0; i < ns; ++i) {
+  for (int i = kPre; i < ns; ++i) {
     const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = fmaf(wi, op[(long long)i * D + e], o[e]);

@@ -51,7 +51,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 METRIC = "attention fwd TFLOP/s + decode KV GB/s, as % of MI355X MFMA/HBM peak"
-KERNEL_SOURCES = ("fwd16p.hip", "common.h", "lds.h")
+KERNEL_SOURCES = ("fwd16p_kernel.h", "common.h", "lds.h")
 # the attention kernel of the headline LFM2 prefill call: the software-pipelined
 # kernel of unmasked, unsplit launches (template arguments: element type, head
 # dim, query heads per workgroup, causal, fused query RoPE, query blocks per wave)

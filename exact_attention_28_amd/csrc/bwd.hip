@@ -31,6 +31,10 @@
 //    memory, and dQ^T += K^T dS^T.
 // Q and K arrive already rotated (the caller stages them); the epilogues of
 // dK and dQ apply the inverse rotation in fp64.
+// Both streaming kernels double-buffer their LDS tiles; ONEBUF instances (a
+// check of that ordering) use one buffer, refilled after a barrier behind its
+// last read, with the same arithmetic in the same order: bit-identical
+// gradients.
 
 #include <type_traits>
 
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const u16* __restrict__ O
 
 // ---------------------------------------------------------------- dK, dV --
 
-template <typename T, bool CAUSAL, bool ROPE>
+template <typename T, bool CAUSAL, bool ROPE, bool ONEBUF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ ndelta,
@@ -340,18 +344,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // the second buffers (the first ones again in ONEBUF instances, refilled
+  // once every wave is done with them)
+  u16* const Qb1 = ONEBUF ? Qs0 : Qs1;
+  u16* const Ob1 = ONEBUF ? Os0 : Os1;
+  float* const Lb1 = ONEBUF ? Ls0 : Ls1;
+  float* const Db1 = ONEBUF ? Ds0 : Ds1;
   for (int it = 0; it < n_it; it += 2) {
     // the next tile goes into the other buffers, last read in the previous step
     float x = stat_load(it + 1);
-    if (it + 1 < n_it) dma(it + 1, Qs1, Os1);
+    if (!ONEBUF && it + 1 < n_it) dma(it + 1, Qb1, Ob1);
     tile(it, Qs0, Os0, Ls0, Ds0);
-    stat_store(x, Ls1, Ds1);
+    if (ONEBUF) {
+      __syncthreads();
+      if (it + 1 < n_it) dma(it + 1, Qb1, Ob1);
+    }
+    stat_store(x, Lb1, Db1);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (it + 1 >= n_it) break;
     x = stat_load(it + 2);
-    if (it + 2 < n_it) dma(it + 2, Qs0, Os0);
-    tile(it + 1, Qs1, Os1, Ls1, Ds1);
+    if (!ONEBUF && it + 2 < n_it) dma(it + 2, Qs0, Os0);
+    tile(it + 1, Qb1, Ob1, Lb1, Db1);
+    if (ONEBUF) {
+      __syncthreads();
+      if (it + 2 < n_it) dma(it + 2, Qs0, Os0);
+    }
     stat_store(x, Ls0, Ds0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
@@ -366,7 +384,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // ---------------------------------------------------------------- dQ --
 
-template <typename T, int HPW, bool CAUSAL, bool ROPE>
+template <typename T, int HPW, bool CAUSAL, bool ROPE, bool ONEBUF>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ ndelta,
@@ -504,14 +522,26 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   if (ntiles > 0) dma(0, Ks0, Vs0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // the second buffers (the first ones again in ONEBUF instances, refilled
+  // once every wave is done with them)
+  u16* const Kb1 = ONEBUF ? Ks0 : Ks1;
+  u16* const Vb1 = ONEBUF ? Vs0 : Vs1;
   for (int t = 0; t < ntiles; t += 2) {
-    if (t + 1 < ntiles) dma(t + 1, Ks1, Vs1);
+    if (!ONEBUF && t + 1 < ntiles) dma(t + 1, Kb1, Vb1);
     tile(t, Ks0, Vs0);
+    if (ONEBUF) {
+      __syncthreads();
+      if (t + 1 < ntiles) dma(t + 1, Kb1, Vb1);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (t + 1 >= ntiles) break;
-    if (t + 2 < ntiles) dma(t + 2, Ks0, Vs0);
-    tile(t + 1, Ks1, Vs1);
+    if (!ONEBUF && t + 2 < ntiles) dma(t + 2, Ks0, Vs0);
+    tile(t + 1, Kb1, Vb1);
+    if (ONEBUF) {
+      __syncthreads();
+      if (t + 2 < ntiles) dma(t + 2, Ks0, Vs0);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
@@ -525,7 +555,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 
 namespace {
 
-template <typename T, bool C, bool R>
+template <typename T, bool C, bool R, bool ONEBUF>
 hipError_t go_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                   const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
                   int Skv, float scale, const double2* tab, float* ndelta, float* lse2,
@@ -547,7 +577,7 @@ hipError_t go_bwd(const void* q, const void* k, const void* v, const void* o, co
   const int n_bh_kv = B * Hkv;
   const long long nkv = (long long)((Skv + 127) / 128) * n_bh_kv;
   if (nkv > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  bwd_dkdv_kernel<T, C, R><<<dim3((unsigned)nkv), dim3(256), 0, stream>>>(
+  bwd_dkdv_kernel<T, C, R, ONEBUF><<<dim3((unsigned)nkv), dim3(256), 0, stream>>>(
       Q, Kp, Vp, dO, lse2, ndelta, static_cast<u16*>(dk), static_cast<u16*>(dv), Hq, Hkv, Sq, Skv,
       scale, sl2, tab, n_bh_kv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -560,7 +590,7 @@ hipError_t go_bwd(const void* q, const void* k, const void* v, const void* o, co
     const int n_bh = B * (Hq / HPW);
     const long long nb = (long long)n_qt * n_bh;
     if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    bwd_dq_kernel<T, HPW, C, R><<<dim3((unsigned)nb), dim3(256), 0, stream>>>(
+    bwd_dq_kernel<T, HPW, C, R, ONEBUF><<<dim3((unsigned)nb), dim3(256), 0, stream>>>(
         Q, Kp, Vp, dO, lse2, ndelta, static_cast<u16*>(dq), Hq, Hkv, Sq, Skv, scale, sl2, tab,
         n_qt, n_bh);
     return hipGetLastError();
@@ -601,10 +631,12 @@ hipError_t launch_bwd16(const void* q, const void* k, const void* v, const void*
     qin = qs;
     kin = ks;
   }
-#define XATTN_BWD_CASE(TT, C, R)                                                               \
-  if ((causal != 0) == C && rope == R)                                                         \
-    return go_bwd<TT, C, R>(qin, kin, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, scale, \
-                            rope_tab, ndelta, lse2, stream);
+  const bool onebuf = lds_single_buffer_enabled();
+#define XATTN_BWD_CASE(TT, C, R)                                                                 \
+  if ((causal != 0) == C && rope == R)                                                           \
+    return (onebuf ? go_bwd<TT, C, R, true> : go_bwd<TT, C, R, false>)(                          \
+        qin, kin, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, scale, rope_tab, ndelta, lse2, \
+        stream);
   if (dtype == 1) {
     XATTN_BWD_CASE(__bf16, false, false)
     XATTN_BWD_CASE(__bf16, true, false)

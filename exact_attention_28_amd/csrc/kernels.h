@@ -62,6 +62,12 @@ struct KeySplit {
 // ATTN_FWD_SPLITS in the environment overrides it (clamped to
 // [1, min(16, tiles)]).
 int fwd16_key_splits(int B, int Hq, int Hkv, int Sq, int kv_rows, int D);
+// Merge of key-split partials op [rows, ns, D] fp32 (normalised) and lp
+// [rows, ns] (natural-log LSE) into o [rows, D] (dtype 1 bf16, 2 fp16) and
+// lse [B, Hq, Sq] (nullable); rows = B * Sq * Hq in O's row order.
+hipError_t launch_fwd16_merge(const float* op, const float* lp, void* o, float* lse,
+                              long long rows, int Sq, int Hq, int ns, int D, int dtype,
+                              hipStream_t stream);
 size_t fwd16_split_ws_bytes(int B, int Hq, int Sq, int D, int ns);
 
 // Prefill: q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D], o like q, lse [B,Hq,Sq] (nullable).
@@ -79,14 +85,33 @@ hipError_t launch_fwd16(const void* q, const void* k, const void* v, void* o, fl
                         MaskView mask = MaskView(), KeySplit ks = KeySplit());
 
 // The unmasked, unsplit 16-bit forward with the software-pipelined key loop
-// (fwd16p.hip): same arguments and results as launch_fwd16 without a mask or
-// key splits.  ATTN_FWD_PIPELINE=0 in the environment turns it off
+// (fwd16p_kernel.h): same arguments and results as launch_fwd16 without a
+// mask or key splits.  ATTN_FWD_PIPELINE=0 in the environment turns it off
 // (launch_fwd16 then runs fwd16_kernel for those launches too).
 bool fwd16_pipelined_enabled();
 hipError_t launch_fwd16_pipelined(const void* q, const void* k, const void* v, void* o,
                                   float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
                                   int causal, float scale, const double2* rope_tab, int dtype,
                                   hipStream_t stream, const int* kv_lens, int kv_rows);
+
+// Single-buffer instances of both 16-bit forwards, a check of their LDS
+// double buffering: one K and one V buffer, refilled only after a barrier
+// that follows every wave's last read of it, with the loads waited for before
+// the next read.  Same arguments as launch_fwd16 / launch_fwd16_pipelined and
+// bit-identical results.  launch_fwd16 routes every 16-bit forward through
+// them, and launch_bwd16 its two streaming kernels through their own
+// single-buffer instances, when ATTN_LDS_SINGLE_BUFFER=1 is set in the
+// environment (read per call).
+bool lds_single_buffer_enabled();
+hipError_t launch_fwd16_onebuf(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                               float scale, const double2* rope_tab, int dtype, hipStream_t stream,
+                               const int* kv_lens, int kv_rows, MaskView mask, KeySplit ks);
+hipError_t launch_fwd16_pipelined_onebuf(const void* q, const void* k, const void* v, void* o,
+                                         float* lse, int B, int Hq, int Hkv, int Sq, int Skv,
+                                         int D, int causal, float scale, const double2* rope_tab,
+                                         int dtype, hipStream_t stream, const int* kv_lens,
+                                         int kv_rows);
 
 // Cache append: rows t < Sq of k_new/v_new [B,Sq,Hkv,D] (bf16) go to rows
 // L_b + t of kcache/vcache [B,rows,Hkv,D] with L_b = min(max(lens[b], 0),

@@ -46,6 +46,14 @@
  *    see, so an eager call after a capture builds its table in a new buffer
  *    rather than trusting the cache.  The library's buffers are shared, so
  *    replays must still be ordered with other calls that use them.
+ *  - Environment variables (read on every call): ATTN_DEBUG=1 (host checks of
+ *    device-resident lengths, see attn_decode_splitkv), ATTN_FWD_SPLITS=n
+ *    (see attn_fwd), ATTN_FWD_PIPELINE=0 (unmasked 16-bit forwards run the
+ *    tile kernel instead of the pipelined one; same results up to fp32
+ *    rounding order) and ATTN_LDS_SINGLE_BUFFER=1 (the 16-bit forward and
+ *    backward kernels run with one LDS tile buffer instead of two, each
+ *    refilled only when no wave reads it: slower, bit-identical results; a
+ *    check of the double buffering's waits and barriers).
  */
 #ifndef EXACT_ATTN_H
 #define EXACT_ATTN_H

@@ -56,8 +56,8 @@ KERNEL_SOURCES = ("fwd16p_kernel.h", "common.h", "lds.h")
 # kernel of unmasked, unsplit launches (template arguments: element type, head
 # dim, query heads per workgroup, causal, fused query RoPE, query blocks per wave)
 KERNEL_NAME = "fwdp_kernel"
-KERNEL_LABEL = "fwdp_kernel<__bf16, D=64, HPW=4, CAUSAL=1, ROPE=1, NQB=2>"
-KERNEL_LABEL_NOROPE = "fwdp_kernel<__bf16, D=64, HPW=4, CAUSAL=1, ROPE=0, NQB=2>"
+KERNEL_LABEL = "fwdp_kernel<__bf16, D=64, HPW=4, CAUSAL=1, ROPE=1, NQB=2, KS=1, ONEBUF=0>"
+KERNEL_LABEL_NOROPE = "fwdp_kernel<__bf16, D=64, HPW=4, CAUSAL=1, ROPE=0, NQB=2, KS=1, ONEBUF=0>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwdp_lfm2_gqa_prefill_s4096_traffic.txt")
 
 

@@ -313,6 +313,7 @@ def test_decode_variants(case):
     for ns in splits:
         ws = torch.empty(xa.attn_decode_workspace_bytes(B, Hq, D, ns), dtype=torch.uint8,
                          device=DEV)
+        outs = []  # library-owned and caller workspace: the same bits
         for workspace in (None, ws):
             o, lse = xa.attn_decode_splitkv(dq, dk, dv, dsl, ns, scale=cfg.scale,
                                             workspace=workspace)
@@ -321,6 +322,9 @@ def test_decode_variants(case):
             empty = sl == 0
             assert (og[empty] == 0).all() and np.isneginf(lg[empty]).all()
             check_bf16(og, lg, o_ref, lse_ref, f"{case} ns={ns}")
+            outs.append((o.view(torch.int16).cpu().numpy(), lse.cpu().numpy()))
+        np.testing.assert_array_equal(outs[0][0], outs[1][0])
+        np.testing.assert_array_equal(outs[0][1].view(np.int32), outs[1][1].view(np.int32))
 
 
 def test_decode_equals_last_prefill_row():

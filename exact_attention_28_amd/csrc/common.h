@@ -116,6 +116,18 @@ __device__ __forceinline__ void rotate_pair(double x0, double x1, double2 cs, do
   r1 = x0 * cs.y + x1 * cs.x;
 }
 
+// fp64 -> bf16 through fp32 (v_cvt_f32_f64, then the packing instruction, both
+// nearest with ties to even) rounds twice.  That equals the single rounding of
+// f64_to_bf16_bits except when the fp32 value is itself a bf16 midpoint: every
+// bf16 midpoint is an fp32 value, so the fp32 value nearest to x lies on the
+// same side of each midpoint as x unless it is one.  bf16_mid_key(f) is 0
+// exactly for a midpoint (low 16 bits 0x8000); callers take the minimum over
+// their values, convert through fp32, and redo with f64_to_bf16_bits when it
+// is 0.
+__device__ __forceinline__ uint32_t bf16_mid_key(float f) {
+  return (__float_as_uint(f) ^ 0x8000u) & 0xffffu;
+}
+
 // Sum over groups of N consecutive lanes (N in 2,4,8,16) with DPP moves.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {

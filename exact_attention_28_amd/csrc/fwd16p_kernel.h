@@ -277,17 +277,37 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     }
     if constexpr (ROPE) {
+      // bf16: the rotated values go to bf16 through fp32 (bf16_mid_key); the
+      // rare group of 8 values with one on a bf16 midpoint is redone with the
+      // single rounding by the whole wave, so the result is that rounding's
+      constexpr bool VIA32 = std::is_same<T, __bf16>::value;
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
+        for (int ks = 0; ks < NKS; ++ks) {
+          const u32x4 raw = qw[qb][ks];
+          double r0[4], r1[4];
+          uint32_t mid = 1;  // 0 once a value lands on a bf16 midpoint
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            double r0, r1;
-            rotate_pair((double)F::lo(qw[qb][ks][e]), (double)F::hi(qw[qb][ks][e]),
-                        cs[qb][ks][e], r0, r1);
-            qw[qb][ks][e] = F::from_f64(r0) | (F::from_f64(r1) << 16);
+            rotate_pair((double)F::lo(raw[e]), (double)F::hi(raw[e]), cs[qb][ks][e], r0[e], r1[e]);
+            if constexpr (VIA32) {
+              float f0 = (float)r0[e], f1 = (float)r1[e];
+              // (opaque: the compiler would fuse the two conversions into its own
+              // single-rounding sequence, which costs more)
+              asm("" : "+v"(f0), "+v"(f1));
+              mid = min(mid, min(bf16_mid_key(f0), bf16_mid_key(f1)));
+              qw[qb][ks][e] = F::pack(f0, f1);
+            } else {
+              qw[qb][ks][e] = F::from_f64(r0[e]) | (F::from_f64(r1[e]) << 16);
+            }
           }
+          if (VIA32 && __builtin_amdgcn_ballot_w64(mid == 0)) {  // wave-uniform, rare
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              qw[qb][ks][e] = F::from_f64(r0[e]) | (F::from_f64(r1[e]) << 16);
+          }
+        }
     }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)

@@ -9,6 +9,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace xattn {
 
 // Row t of the table holds (cos, sin) of theta = (pos0 + t) / base^(2i/D), i < D/2.
@@ -109,12 +111,30 @@ __global__ void rope_rotate_qk16(const u16* __restrict__ q, u16* __restrict__ qo
       const int part = c % cpr;
       const u32x4 w = *reinterpret_cast<const u32x4*>(x + (long long)c * 8);
       u32x4 r;
+      // bf16: through fp32 (bf16_mid_key), the rare chunk with a value on a
+      // bf16 midpoint redone with the single rounding
+      constexpr bool VIA32 = std::is_same<T, __bf16>::value;
+      double r0[4], r1[4];
+      uint32_t mid = 1;  // 0 once a value lands on a bf16 midpoint
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        double r0, r1;
         rotate_pair((double)Fmt16<T>::lo(w[e]), (double)Fmt16<T>::hi(w[e]), trow[part * 4 + e],
-                    r0, r1);
-        r[e] = Fmt16<T>::from_f64(r0) | (Fmt16<T>::from_f64(r1) << 16);
+                    r0[e], r1[e]);
+        if constexpr (VIA32) {
+          float f0 = (float)r0[e], f1 = (float)r1[e];
+          // (opaque: the compiler would fuse the two conversions into its own
+          // single-rounding sequence, which costs more)
+          asm("" : "+v"(f0), "+v"(f1));
+          mid = min(mid, min(bf16_mid_key(f0), bf16_mid_key(f1)));
+          r[e] = Fmt16<T>::pack(f0, f1);
+        } else {
+          r[e] = Fmt16<T>::from_f64(r0[e]) | (Fmt16<T>::from_f64(r1[e]) << 16);
+        }
+      }
+      if (VIA32 && mid == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          r[e] = Fmt16<T>::from_f64(r0[e]) | (Fmt16<T>::from_f64(r1[e]) << 16);
       }
       *reinterpret_cast<u32x4*>(y + (long long)c * 8) = r;
     }

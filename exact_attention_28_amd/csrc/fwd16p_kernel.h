@@ -70,22 +70,28 @@ namespace xattn {
 // A lane's sum of probabilities over a half above which the reference moves.
 constexpr float kRefWindow = 0x1p8f;
 
+// Query waves per key group: 4, or 2 in the four-group instances (KS = 4).
+template <int KS>
+constexpr int fwdp_query_waves() { return KS == 4 ? 2 : 4; }
+
 template <typename T, int D, int HPW, bool CAUSAL, bool ROPE, int NQB, int KS, bool ONEBUF>
-__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2))) void fwdp_kernel(
+__global__ __launch_bounds__(64 * fwdp_query_waves<KS>() * KS)
+__attribute__((amdgpu_waves_per_eu(2))) void fwdp_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Sq, int Skv_all,
     const int* __restrict__ kv_lens, int kv_rows, float scale_log2,
     const double2* __restrict__ tab, int n_qt, int n_bh) {
-  constexpr int BM = 128 * NQB, BN = 64, NP = BM / HPW;
-  constexpr int KCH = D / 8;          // 16-byte chunks per row
-  constexpr int LD = BN * KCH / 256;  // 16-byte chunks per thread per tile (K and V each)
+  constexpr int QW = fwdp_query_waves<KS>();  // waves of a key group
+  constexpr int BM = 32 * QW * NQB, BN = 64, NP = BM / HPW;
+  constexpr int KCH = D / 8;                // 16-byte chunks per row
+  constexpr int LD = BN * KCH / (64 * QW);  // 16-byte chunks per thread per tile (K and V each)
   constexpr int NDB = D / 32;         // 32-row blocks of O^T
   constexpr int NKS = D / 16;         // k-steps of the QK^T contraction
   static_assert(LD >= 1, "tile loads");
   typedef Fmt16<T> F;
   typedef typename F::v8 v8;
 
-  // K and V double buffers of each key group (KS groups of 4 waves; see below)
+  // K and V double buffers of each key group (KS groups of QW waves; see below)
   __shared__ __attribute__((aligned(16))) u16 Ks0g[KS][BN * D];
   __shared__ __attribute__((aligned(16))) u16 Vs0g[KS][BN * D];
   __shared__ __attribute__((aligned(16))) u16 Ks1g[KS][BN * D];
@@ -98,14 +104,14 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2))) v
                            (NP * D / 2) % 256 == 0;
   __shared__ __attribute__((aligned(16))) double2 Ts[TAB_LDS ? NP * (D / 2) : 1];
 
-  // KS = 2 (launches with fewer workgroups than CUs): two groups of 4 waves
-  // take the two halves of the workgroup's key tiles for the same query
-  // columns, with their own K/V buffers, and merge (m, l, O) through LDS at
-  // the end.  Both groups run the same number of pairs (the second group's
-  // last tiles may lie past the keys: range-checked loads read zeros there
-  // and the mask drops them), so they meet at every barrier.
-  const int tid = threadIdx.x, lane = tid & 63, w = (tid >> 6) & 3;
-  const int grp = KS > 1 ? (tid >> 8) : 0;
+  // KS = 2 or 4 (launches with fewer workgroups than CUs): KS groups of QW
+  // waves take KS consecutive ranges of the workgroup's key tiles for the
+  // same query columns, with their own K/V buffers, and merge (m, l, O)
+  // through LDS at the end.  Every group runs the same number of pairs (the
+  // last groups' last tiles may lie past the keys: range-checked loads read
+  // zeros there and the mask drops them), so they meet at every barrier.
+  const int tid = threadIdx.x, lane = tid & 63, w = (tid >> 6) % QW;
+  const int grp = KS > 1 ? (tid >> 6) / QW : 0;
   const int c = lane & 31, g = lane >> 5;
   u16* const Ks0 = Ks0g[grp];
   u16* const Vs0 = Vs0g[grp];
@@ -606,7 +612,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2))) v
     pv(vlast, 1, pB);
   }
 
-  if constexpr (KS > 1) {
+  if constexpr (KS == 2) {
     // the second key group's (m, l, O) into the first's: lane (w, lane) of
     // both groups holds the same query column.  The exchange reuses the K/V
     // buffers once every wave's last reads of them are done: O block db of
@@ -644,6 +650,56 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2))) v
       m_run[0] = mn;
     }
   }
+  if constexpr (KS == 4) {
+    // groups 1..3 store (m, l, O) in the K/V buffers once every wave's last
+    // reads of them are done (group i in Ks0g, Vs0g, Ks1g: O block db of
+    // the group's QW waves at float (16 db + r) * 64 QW + 64 w + lane, then m
+    // and l), and group 0 merges the four with one common maximum.
+    static_assert(NQB == 1 && !ROPE, "key groups");
+    constexpr int XW = 64 * QW;  // lanes of a group
+    static_assert((NDB * 16 + 2) * XW * 4 <= (int)sizeof(Ks0g), "exchange space");
+    auto xg = [&](int i) -> float* {  // exchange area of group i + 1
+      return reinterpret_cast<float*>(i == 0 ? &Ks0g[0][0] : (i == 1 ? &Vs0g[0][0] : &Ks1g[0][0]));
+    };
+    const int xl = w * 64 + lane;
+    __syncthreads();
+    if (grp > 0) {
+      float* const x = xg(grp - 1);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[(16 * db + r) * XW + xl] = oacc[0][db][r];
+      x[NDB * 16 * XW + xl] = m_run[0];
+      x[(NDB * 16 + 1) * XW + xl] = l_run[0];
+    }
+    __syncthreads();
+    if (grp == 0) {
+      float mi[4], li[4];
+      mi[0] = m_run[0];
+      li[0] = l_run[0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) {
+        mi[i] = xg(i - 1)[NDB * 16 * XW + xl];
+        li[i] = xg(i - 1)[(NDB * 16 + 1) * XW + xl];
+      }
+      const float mn = fmaxf(fmaxf(mi[0], mi[1]), fmaxf(mi[2], mi[3]));
+      float a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = (mn == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi[i] - mn);
+      l_run[0] = li[0] * a[0] + li[1] * a[1] + li[2] * a[2] + li[3] * a[3];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float acc = oacc[0][db][r] * a[0];
+#pragma unroll
+          for (int i = 1; i < 4; ++i) acc += xg(i - 1)[(16 * db + r) * XW + xl] * a[i];
+          oacc[0][db][r] = acc;
+        }
+      m_run[0] = mn;
+    }
+  }
   if (KS > 1 && grp != 0) return;
 
 #pragma unroll
@@ -675,12 +731,13 @@ template <bool ONEBUF, typename T, int D, int HPW, bool CAUSAL, bool ROPE, int N
 static hipError_t gop(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int Hq, int Hkv, int Sq, int Skv, const int* kv_lens, int kv_rows,
                       float scale, const double2* tab, hipStream_t stream) {
-  constexpr int NP = 128 * NQB / HPW;
+  constexpr int NP = 32 * fwdp_query_waves<KS>() * NQB / HPW;
   const int n_qt = (Sq + NP - 1) / NP;
   const int n_bh = B * (Hq / HPW);
   const long long nblocks = (long long)n_qt * n_bh;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  launch_kernel(fwdp_kernel<T, D, HPW, CAUSAL, ROPE, NQB, KS, ONEBUF>, dim3((unsigned)nblocks), dim3(256 * KS),
+  launch_kernel(fwdp_kernel<T, D, HPW, CAUSAL, ROPE, NQB, KS, ONEBUF>, dim3((unsigned)nblocks),
+                dim3(64 * fwdp_query_waves<KS>() * KS),
                 stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
                 static_cast<const u16*>(v), static_cast<u16*>(o), lse, Hq, Hkv, Sq, Skv, kv_lens,
                 kv_rows, scale * kLog2e, tab, n_qt, n_bh);
@@ -705,6 +762,15 @@ static hipError_t gop_nqb(const void* q, const void* k, const void* v, void* o, 
   // second group's prologue cost more than the halved loop saves (1024 query
   // rows, 8 heads: 512 keys 12.5 -> 13.1 us, 1024 keys 17.3 -> 14.5 us)
   if constexpr (!ROPE) {
+    // one head per workgroup at D = 64 with at most one 64-query workgroup
+    // per CU: four key groups of two waves (64 query rows), so the launch
+    // covers up to every CU rather than half of them
+    if constexpr (D == 64 && HPW == 1) {
+      const long long wg64 = (long long)((Sq + 63) / 64) * B * Hq;
+      if (wg64 <= 256 && Skv >= 16 * 64)
+        return gop<ONEBUF, T, D, HPW, CAUSAL, ROPE, 1, 4>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv,
+                                                          kv_lens, kv_rows, scale, tab, stream);
+    }
     const long long wg1 = (long long)((Sq + 128 / HPW - 1) / (128 / HPW)) * B * (Hq / HPW);
     if (wg1 < 256 && Skv >= 16 * 64)
       return gop<ONEBUF, T, D, HPW, CAUSAL, ROPE, 1, 2>(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, kv_lens,

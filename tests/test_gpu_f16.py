@@ -65,6 +65,7 @@ F16_CASES = [  # B, Hq, Hkv, Sq, Skv, D, causal, rope
     (2, 6, 3, 33, 90, 40, False, 10000.0),    # padded head dim
     (4, 4, 4, 600, 600, 64, False, 0.0),      # two query blocks per wave
     (1, 4, 2, 150, 1090, 64, True, 0.0),      # two key groups per workgroup
+    (1, 3, 3, 150, 1090, 64, True, 0.0),      # four key groups of two waves
 ]
 
 

@@ -69,6 +69,8 @@ UNMASKED = [  # B, Hq, Hkv, Sq, Skv, D, causal, rope, dtype, env
     (1, 4, 4, 200, 1100, 128, False, 0.0, torch.bfloat16, {}),       # two key groups
     (1, 4, 2, 150, 1090, 64, True, 0.0, torch.float16, {}),          # two key groups, causal, fp16
     (1, 6, 2, 77, 190, 64, False, 0.0, torch.float16, {}),           # 1 head per workgroup
+    (1, 4, 4, 200, 1100, 64, False, 0.0, torch.bfloat16, {}),        # four key groups
+    (1, 3, 1, 150, 1090, 64, True, 0.0, torch.float16, {}),          # four key groups, causal, fp16
     (2, 32, 8, 2048, 2048, 64, True, 10000.0, torch.bfloat16,        # tile kernel, 2 blocks/wave
      {"ATTN_FWD_PIPELINE": "0"}),
     (1, 8, 2, 160, 600, 128, False, 10000.0, torch.bfloat16,         # tile kernel, D 128

@@ -148,12 +148,16 @@ BF16_CASES = [  # B, Hq, Hkv, Sq, Skv, D, causal, rope, amplitude
     (64, 1, 1, 33, 33, 64, True, 0.0, 1.0),     # many small (batch, head) units
     (1, 12, 2, 100, 100, 128, True, 10000.0, 1.0),  # 6 query heads per kv head (pairs of heads)
     # under-filled launches with >= 16 key tiles: two key groups per workgroup
-    # merged through LDS (odd tile counts leave the second group a tile past
-    # the keys; causal rows see only part of the second group's keys)
+    # (four of two waves for one head per workgroup at D 64) merged through
+    # LDS (tile counts that do not divide leave the last groups tiles past
+    # the keys; causal rows see only part of the later groups' keys)
     (1, 4, 2, 200, 1100, 64, False, 0.0, 1.0),
-    (1, 4, 4, 150, 1050, 64, True, 0.0, 1.0),
+    (1, 4, 4, 150, 1050, 64, True, 0.0, 1.0),     # four groups
     (2, 4, 4, 100, 1300, 128, False, 0.0, 1.0),
     (1, 4, 1, 64, 1024, 64, True, 0.0, 4.0),
+    (1, 4, 4, 200, 1100, 64, False, 0.0, 1.0),    # four groups, 18 tiles
+    (1, 3, 1, 100, 1500, 64, True, 0.0, 4.0),     # four groups, bottom-right causal
+    (2, 2, 2, 1, 1025, 64, True, 0.0, 1.0),       # four groups, one query row
 ]
 
 

@@ -39,12 +39,17 @@ def _bits(x):
     return W.f32_to_bf16_bits(x)
 
 
-@pytest.mark.parametrize("D,Hq,Hkv,causal,rope", [(64, 8, 2, True, 10000.0),
-                                                  (128, 4, 4, False, 0.0),
-                                                  (64, 12, 4, True, 500.0)])
-def test_chunked_prefill_serving_loop(D, Hq, Hkv, causal, rope):
-    say("case kvcache", D, Hq, Hkv, causal, rope)
-    B, Smax = 2, 320
+@pytest.mark.parametrize("D,Hq,Hkv,causal,rope,Smax", [
+    (64, 8, 2, True, 10000.0, 320),
+    (128, 4, 4, False, 0.0, 320),
+    (64, 12, 4, True, 500.0, 320),
+    # caches of >= 16 key tiles: one head per workgroup at D 64 takes four key
+    # groups (sized by the cache, most of whose rows are not yet written)
+    (64, 4, 4, False, 0.0, 1100),
+    (64, 3, 3, True, 0.0, 1100)])
+def test_chunked_prefill_serving_loop(D, Hq, Hkv, causal, rope, Smax):
+    say("case kvcache", D, Hq, Hkv, causal, rope, Smax)
+    B = 2
     chunks = [57, 100, 64, 1, 1, 33]
     prefix = [0, 20]
     total = [prefix[b] + sum(chunks) for b in range(B)]

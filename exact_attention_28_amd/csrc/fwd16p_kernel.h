@@ -12,7 +12,8 @@
 // (scirs2-neural 0.4.4 src/layers/grouped_query_attention.rs forward loop).
 //
 // Layout and tiling are those of fwd16_kernel (fwd16_kernel.h): a workgroup of 4
-// waves owns 128 * NQB query columns (HPW heads of one kv head x positions),
+// waves owns 128 * NQB query columns (HPW heads of one kv head x positions;
+// under-filled launches add key groups, see KS below),
 // S^T = K Q^T and O^T += V^T P^T on the 32x32x16 matrix instructions, K and V
 // tiles of 64 keys in XOR-swizzled LDS filled by direct HBM->LDS loads.  What
 // differs is the order of work inside a wave.  Keys are consumed in halves of

@@ -621,8 +621,15 @@ __attribute__((amdgpu_waves_per_eu(2))) void fwdp_kernel(
     // epilogue: softmax of the last half with the PV of the one before, then
     // the PV of the last half (V tile nt-1 in buffer (nt-1) & 1)
     const u16* vlast = ((nt - 1) & 1) ? Vb1 : Vs0;
-    step(Y, sB, kbase + (nt - 1) * BN + 32, pB, N, sA, Ks0, 0, Y, pA, vlast, 0);
-    pv(vlast, 1, pB);
+    // (the last half's softmax and PV products are left out when it lies
+    // wholly past the keys every query of the workgroup sees: Skv mod 64 in
+    // 1..32; their probabilities would all be 0)
+    if (KS == 1 && nt >= 2 && (t0 + nt - 1) * BN + 32 >= kv_end) {
+      pv(vlast, 0, pA);
+    } else {
+      step(Y, sB, kbase + (nt - 1) * BN + 32, pB, N, sA, Ks0, 0, Y, pA, vlast, 0);
+      pv(vlast, 1, pB);
+    }
   }
 
   if constexpr (KS == 2) {
